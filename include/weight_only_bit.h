@@ -1,0 +1,165 @@
+/*
+ * weight_only_bit -- MI355X (gfx950) weight-only 4-bit GEMM library, C ABI.
+ *
+ *     Y[M,N] = X[M,K] . dequant(Wq)[N,K]^T
+ *
+ * Two weight formats:
+ *  - W4A16: unsigned 4-bit codes q, a scale s per (row, group of g along K) in
+ *    the activation dtype and an unsigned 4-bit zero-point z per (row, group);
+ *    w = (q - z) * s.  Source: "Keep W4A16 zero-points packed at 4 bits instead
+ *    of expanding to 2 bytes" (ROCm/vllm pull request 1073), sections Problem
+ *    and Change: the skinny W4A16 GEMM takes the zero-points packed eight per
+ *    int32 along N and extracts the nibble of row n from word n/8 at bits
+ *    4*(n%8); activation-dtype zero-points are rejected rather than
+ *    reinterpreted (section Testing).
+ *  - MXFP4 (OCP MX E2M1 elements, one E8M0 scale per 32 along K) for MoE
+ *    stage 1 with BF16 activations.  Source: "Add BF16xFP4 MoE GEMM stage1
+ *    kernel" (ROCm/FlyDSL pull request 424), summary and Technical Details: the
+ *    FP4 weights are dequantized to BF16 in software (one scaled conversion per
+ *    byte, two elements each) before each BF16 matrix-core multiply; the E8M0
+ *    byte is the binary32 exponent of the scale; the store guard keeps
+ *    out-of-range tiles from writing into neighbouring token-slot rows.
+ *
+ * Layouts (all row-major, contiguous, device memory unless stated):
+ *   x        [M][K]        activation dtype (WOB_F16 or WOB_BF16)
+ *   qweight  [N][K/8]      int32; code of (n, k) is bits 4*(k%8) of word (n, k/8)
+ *   scales   [N][K/g]      activation dtype (must equal x's dtype)
+ *   qzeros   [N/8][K/g]    int32; zero-point of (n, j) is bits 4*(n%8) of word (n/8, j)
+ *                          NULL means symmetric codes: z = 8 for every group
+ *   y        [M][N]        activation dtype, rounded to nearest even from fp32
+ *   w_fp4    [E][N][K/2]   uint8; element k is the low nibble of byte k/2 when
+ *                          k is even, the high nibble when k is odd
+ *   w_scale  [E][N][K/32]  uint8 E8M0 exponent b; scale = 2^(b-127)
+ * Packed words are unsigned bit containers (logical shifts).
+ *
+ * Conventions shared by every entry point:
+ *  - All pointers are owned by the caller; the library keeps no allocation and
+ *    no state beyond a per-device architecture check.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *    void*, NULL = the null stream); nothing synchronizes.
+ *  - Every argument is validated before any device call; on a non-zero status
+ *    nothing was enqueued.  No exception crosses the ABI.
+ *  - Device pointers must be 16-byte aligned.
+ *  - Results are deterministic for a fixed shape: the summation order over K
+ *    does not depend on timing.
+ */
+#ifndef WEIGHT_ONLY_BIT_H
+#define WEIGHT_ONLY_BIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define WOB_OK 0
+#define WOB_INVALID_ARG 1 /* null pointer, bad shape, misalignment, small workspace */
+#define WOB_DTYPE 2       /* a dtype tag the operand cannot have (e.g. act-dtype zero-points) */
+#define WOB_UNSUPPORTED 3 /* device is not gfx950, or a group size the kernels do not take */
+#define WOB_HIP 4         /* the HIP runtime reported an error at launch */
+
+/* Dtype tags. */
+#define WOB_F16 0
+#define WOB_BF16 1
+#define WOB_U4X8_I32 2 /* eight 4-bit values packed in an int32 */
+#define WOB_F32 3
+
+/* Kernel path selection for w4a16_gemm_ex. */
+#define WOB_PATH_AUTO 0   /* M <= 8 (and X fits the skinny kernel's LDS) -> skinny, else tiled */
+#define WOB_PATH_SKINNY 1 /* split-K GEMV; requires M <= 8 */
+#define WOB_PATH_TILED 2  /* cooperative-tile MFMA GEMM; any M >= 1 */
+
+/* Text of a status code (static storage). */
+const char *wob_status_str(int status);
+
+/* Detail of the last non-OK status returned on this thread (static/thread-local storage). */
+const char *wob_last_error(void);
+
+/*
+ * Check that the current HIP device is gfx950.  Returns WOB_OK or
+ * WOB_UNSUPPORTED (WOB_HIP if the runtime cannot be queried).
+ */
+int wob_device_check(void);
+
+/*
+ * W4A16 GEMM: y[m][n] = sum_k x[m][k] * (q(n,k) - z(n,k/g)) * s(n,k/g).
+ * Source: zero-point page above, sections Problem and Change (packed
+ * zero-points, nibble extraction inside the kernel).
+ *
+ *  x_dtype, scales_dtype: WOB_F16 or WOB_BF16 and equal, else WOB_DTYPE.
+ *  zeros_dtype: WOB_U4X8_I32 (ignored when qzeros == NULL); any other tag
+ *    -> WOB_DTYPE (activation-dtype zero-points are refused, not reinterpreted).
+ *  group_size in {32, 64, 128} (else WOB_UNSUPPORTED); K % group_size == 0,
+ *    K % 32 == 0, N % 8 == 0, M >= 0, N >= 0, K >= 32 (else WOB_INVALID_ARG).
+ *    M == 0 or N == 0 is a no-op returning WOB_OK.
+ *  Accumulation is fp32; y is rounded to nearest even in x's dtype.
+ */
+int w4a16_gemm(const void *x, int x_dtype, const int32_t *qweight, const void *scales,
+               int scales_dtype, const void *qzeros, int zeros_dtype, void *y, int64_t M,
+               int64_t N, int64_t K, int64_t group_size, void *stream);
+
+/* As w4a16_gemm with an explicit kernel path (WOB_PATH_*). */
+int w4a16_gemm_ex(const void *x, int x_dtype, const int32_t *qweight, const void *scales,
+                  int scales_dtype, const void *qzeros, int zeros_dtype, void *y, int64_t M,
+                  int64_t N, int64_t K, int64_t group_size, int path, void *stream);
+
+/*
+ * Ragged grouped W4A16 GEMM ("contiguous grouped" form): group e owns rows
+ * [m_offsets[e], m_offsets[e+1]) of x[total_M][K] and y[total_M][N] and uses
+ * its own weights qweight[e][N][K/8], scales[e][N][K/g], qzeros[e][N/8][K/g]
+ * (qzeros may be NULL: symmetric).  m_offsets is a DEVICE int64 array of
+ * num_groups+1 entries that must be nondecreasing from 0 to total_M (a
+ * precondition; the kernel clamps every range to [0, total_M]).  Rows outside
+ * every group are not written.  Same dtype and shape rules as w4a16_gemm.
+ * Source: the grouped GEMM named on "ROCm IQ4_XS keep-quant GEMM is 8.8x
+ * behind llama.cpp's WMMA path" (vllm.cpp issue 3006), section What already
+ * exists; the ragged-offset reading is this library's.
+ */
+int w4a16_gemm_grouped(const void *x, int x_dtype, const int64_t *m_offsets, int64_t num_groups,
+                       int64_t total_M, const int32_t *qweight, const void *scales,
+                       int scales_dtype, const void *qzeros, int zeros_dtype, void *y, int64_t N,
+                       int64_t K, int64_t group_size, void *stream);
+
+/* Bytes of device workspace mxfp4_moe_gemm needs for T tokens, topk slots, E experts. */
+size_t mxfp4_moe_gemm_workspace_size(int64_t T, int64_t topk, int64_t E);
+
+/*
+ * MoE stage 1, BF16 x MXFP4: for token t and slot s with expert e = topk_ids[t][s],
+ *   y[t][s][n] = sum_k x[t][k] * e2m1(code_e(n,k)) * 2^(w_scale[e][n][k/32] - 127)
+ * (pre-activation; gate and up halves of N as stored; no routing-weight
+ * multiply).  Source: MXFP4 page above, summary and Technical Details.
+ *
+ *  x [T][K] bf16; topk_ids [T][topk] int32 on the device; y [T][topk][N] bf16.
+ *  Rows whose id lies outside [0, E) are written as zeros.
+ *  K % 32 == 0, K >= 32, N % 16 == 0, T >= 0, 1 <= topk, 1 <= E (else WOB_INVALID_ARG).
+ *  workspace: device memory of at least mxfp4_moe_gemm_workspace_size(T, topk, E)
+ *  bytes, 16-byte aligned (else WOB_INVALID_ARG); its contents on entry do not
+ *  matter.  Calls that share one workspace must be ordered on one stream.
+ */
+int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
+                   const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E, int64_t N,
+                   int64_t K, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Dequantization probes: run the same device dequantization helpers the GEMM
+ * kernels use and write the dequantized weights out[N][K].
+ *  out_dtype WOB_F32: the skinny kernel's form, exactly (q - z) * s.
+ *  out_dtype == scales_dtype: the MFMA operand form, (q - z) * s rounded to
+ *    nearest even in that dtype.
+ * Same shape and dtype rules as w4a16_gemm.
+ */
+int w4a16_dequant(const int32_t *qweight, const void *scales, int scales_dtype,
+                  const void *qzeros, int zeros_dtype, void *out, int out_dtype, int64_t N,
+                  int64_t K, int64_t group_size, void *stream);
+
+/* MXFP4 probe: out[N][K] bf16 = the MoE kernel's B-operand values for one expert. */
+int mxfp4_dequant(const uint8_t *w_fp4, const uint8_t *w_scale, void *out, int64_t N, int64_t K,
+                  void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WEIGHT_ONLY_BIT_H */

@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports every entry point its header declares, and
+rejects bad arguments before touching a device (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from weight_only_bit_amd import _lib, build
+    if not os.path.exists(_lib.LIB_PATH):
+        build.build()
+    return _lib
+
+
+def _declared_functions():
+    names = []
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                                text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declarations_are_exported(L):
+    declared = _declared_functions()
+    assert "w4a16_gemm" in declared and "mxfp4_moe_gemm" in declared
+    lib = L.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(L.EXPORTS)
+
+
+def test_status_strings(L):
+    assert L.status_str(0) == "ok"
+    assert "dtype" in L.status_str(2)
+
+
+class _Fake:
+    """16-byte aligned host buffer standing in for device pointers: the
+    library must refuse every case below before dereferencing anything."""
+
+    def __init__(self):
+        self.buf = np.zeros(64, np.uint8)
+        addr = self.buf.ctypes.data
+        self.p = ctypes.c_void_p(addr + (-addr) % 16)
+
+
+def _gemm(L, x=True, xdt=0, sdt=0, zdt=2, zeros=True, M=1, N=8, K=64, g=32, path=0):
+    f = _Fake()
+    p = f.p
+    return L.lib().w4a16_gemm_ex(p if x else None, xdt, p, p, sdt, p if zeros else None, zdt, p,
+                                 M, N, K, g, path, None)
+
+
+def test_act_dtype_zero_points_are_refused(L):
+    assert _gemm(L, zdt=0) == L.DTYPE  # fp16 zero-points
+    assert _gemm(L, zdt=1) == L.DTYPE
+    assert _gemm(L, zdt=3) == L.DTYPE
+    assert "packed" in L.last_error()
+
+
+def test_dtype_checks(L):
+    assert _gemm(L, xdt=3, sdt=3) == L.DTYPE
+    assert _gemm(L, xdt=0, sdt=1) == L.DTYPE
+
+
+def test_shape_checks(L):
+    assert _gemm(L, N=12) == L.INVALID_ARG     # N % 8
+    assert _gemm(L, K=48, g=32) == L.INVALID_ARG  # K % g
+    assert _gemm(L, K=16) == L.INVALID_ARG
+    assert _gemm(L, M=-1) == L.INVALID_ARG
+    assert _gemm(L, g=16) == L.UNSUPPORTED
+    assert _gemm(L, g=256, K=256) == L.UNSUPPORTED
+    assert _gemm(L, x=False) == L.INVALID_ARG
+    assert _gemm(L, path=7) == L.INVALID_ARG
+    assert _gemm(L, M=9, path=L.PATH_SKINNY) == L.INVALID_ARG
+    # empty problems are no-ops
+    assert _gemm(L, M=0) == L.OK
+    assert _gemm(L, N=0) == L.OK
+
+
+def test_misaligned_pointer_refused(L):
+    f = _Fake()
+    bad = ctypes.c_void_p(f.p.value + 2)
+    st = L.lib().w4a16_gemm(bad, 0, f.p, f.p, 0, f.p, 2, f.p, 1, 8, 64, 32, None)
+    assert st == L.INVALID_ARG
+
+
+def test_moe_checks(L):
+    f = _Fake()
+    p = f.p
+    need = L.lib().mxfp4_moe_gemm_workspace_size(1024, 4, 32)
+    assert need > 0
+    assert L.lib().mxfp4_moe_gemm_workspace_size(-1, 4, 32) == 0
+    call = lambda K=64, N=32, ws=need, T=4: L.lib().mxfp4_moe_gemm(p, p, p, p, p, T, 4, 32, N, K, p, ws, None)
+    assert call(K=48) == L.INVALID_ARG
+    assert call(N=24) == L.INVALID_ARG
+    assert call(ws=0) == L.INVALID_ARG
+    assert call(T=0) == L.OK
+
+
+def test_grouped_checks(L):
+    f = _Fake()
+    p = f.p
+    g = lambda E=2, zdt=2: L.lib().w4a16_gemm_grouped(p, 0, p, E, 8, p, p, 0, p, zdt, p, 16, 64, 32, None)
+    assert g(zdt=0) == L.DTYPE
+    assert g(E=-1) == L.INVALID_ARG
+    assert g(E=0) == L.OK
+
+
+def test_probe_checks(L):
+    f = _Fake()
+    p = f.p
+    assert L.lib().w4a16_dequant(p, p, 0, p, 2, p, 1, 8, 64, 32, None) == L.DTYPE  # bf16 out, fp16 scales
+    assert L.lib().mxfp4_dequant(p, p, p, 8, 48, None) == L.INVALID_ARG
+
+
+def test_no_gpu_means_an_error_not_a_fallback(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _gemm(L) in (L.HIP, L.UNSUPPORTED)

@@ -1,0 +1,156 @@
+"""GPU parity of the W4A16 kernels against the oracle (through the C ABI).
+
+Bar (weight-only 4-bit GEMM contract): every output element satisfies
+|y - y_ref| <= 1e-3 + 1e-2 * max|y_ref|, no NaN/Inf; the dequantization
+probes are bit-exact.  The matrix follows the zero-point page's value-level
+tests (section Testing: fp16/bf16 x g32/g128 x three shapes including N = 8,
+one packed word, plus the refusal of activation-dtype zero-points) widened to
+g = 64, symmetric codes, signed two-decade scales and ragged K.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from tests.gpu_util import dev, host_bits, is_nan_bits, require_gpu, torch_mod, w4a16_to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wob():
+    require_gpu()
+    import weight_only_bit_amd as w
+    w.device_check()
+    return w
+
+
+def _run(wob, d, path, sentinel=True):
+    torch = torch_mod()
+    t = w4a16_to_device(d)
+    M, N = d["M"], d["N"]
+    out = torch.empty((M + 2, N), dtype=t["x"].dtype, device="cuda")
+    out.fill_(float("nan"))
+    y = out[1:M + 1]
+    wob.gemm(t["x"], t["qweight"], t["scales"], t["qzeros"], d["g"], out=y, path=path)
+    torch.cuda.synchronize()
+    bits = host_bits(out)
+    if sentinel:
+        # rows outside y must still hold the NaN sentinel (no stray writes)
+        assert np.all(is_nan_bits(bits[0], d["dtype"]))
+        assert np.all(is_nan_bits(bits[M + 1], d["dtype"]))
+    return bits[1:M + 1]
+
+
+def _check(oracle, d, ybits):
+    yref = oracle.w4a16_gemm(d["x"], d["dtype"], d["qweight"], d["scales"], d["qzeros"],
+                             d["M"], d["N"], d["K"], d["g"])
+    y = oracle.act_decode(ybits, d["dtype"])
+    ok, err, bound = oracle.tolerance_ok(y, yref)
+    assert ok, f"max err {err} > bound {bound}"
+    return err, bound
+
+
+SHAPES = [(8, 256), (256, 512), (2048, 2048)]
+
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+def test_skinny_parity_matrix(wob, oracle, dtype, g, N, K, M):
+    d = wl.w4a16_inputs(M, N, K, g, dtype, seed=M * 7 + g + N)
+    _check(oracle, d, _run(wob, d, wob.PATH_SKINNY))
+
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("M,N,K,g", [(1, 8, 32, 32), (3, 16, 96, 32), (4, 24, 160, 32),
+                                     (2, 40, 384, 128), (8, 64, 1088, 64), (1, 4104, 4096, 128)])
+def test_skinny_ragged_shapes(wob, oracle, dtype, M, N, K, g):
+    d = wl.w4a16_inputs(M, N, K, g, dtype, seed=N + K)
+    _check(oracle, d, _run(wob, d, wob.PATH_SKINNY))
+
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("M", [1, 4])
+def test_skinny_symmetric_and_signed_scales(wob, oracle, dtype, M):
+    d = wl.w4a16_inputs(M, 256, 1024, 32, dtype, seed=3, symmetric=True)
+    _check(oracle, d, _run(wob, d, wob.PATH_SKINNY))
+    d = wl.w4a16_inputs(M, 256, 1024, 128, dtype, seed=4, signed_scales=True)
+    _check(oracle, d, _run(wob, d, wob.PATH_SKINNY))
+
+
+def test_config_tiny_gemv(wob, oracle):
+    d = wl.BY_KEY["tiny_gemv"].make()
+    _check(oracle, d, _run(wob, d, wob.PATH_AUTO))
+
+
+def test_config_small_batch(wob, oracle):
+    d = wl.BY_KEY["small_batch"].make()
+    _check(oracle, d, _run(wob, d, wob.PATH_AUTO))
+
+
+def test_config_decode_gemv_full_size(wob, oracle):
+    """1x43008x5376 g=32 at full size: every output finite, 4096 sampled outputs
+    (including both ends) against the oracle."""
+    d = wl.BY_KEY["decode_gemv"].make()
+    ybits = _run(wob, d, wob.PATH_AUTO, sentinel=True)
+    y = oracle.act_decode(ybits, d["dtype"])
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(0)
+    ns = np.unique(np.concatenate([[0, 1, 7, 8, d["N"] - 1], rng.integers(0, d["N"], 4096)]))
+    ms = np.zeros_like(ns)
+    yref = oracle.w4a16_gemm_sampled(d["x"], d["dtype"], d["qweight"], d["scales"], d["qzeros"],
+                                     d["K"], d["g"], ms, ns)
+    ok, err, bound = oracle.tolerance_ok(y[ms, ns], yref)
+    assert ok, (err, bound)
+
+
+def test_refuses_act_dtype_zero_points(wob):
+    torch = torch_mod()
+    d = wl.w4a16_inputs(1, 16, 64, 32, wl.F16)
+    t = w4a16_to_device(d)
+    zp_act = torch.zeros((16, 2), dtype=torch.float16, device="cuda")
+    with pytest.raises(TypeError):
+        wob.gemm(t["x"], t["qweight"], t["scales"], zp_act, 32)
+
+
+def test_deterministic_repeat(wob):
+    d = wl.w4a16_inputs(4, 2048, 2048, 128, wl.BF16, seed=1)
+    a = _run(wob, d, wob.PATH_AUTO)
+    b = _run(wob, d, wob.PATH_AUTO)
+    assert np.array_equal(a, b)
+
+
+# --- dequantization probes: bit-exact ---------------------------------------
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("variant", ["asym", "sym", "signed"])
+def test_dequant_probe_bit_exact(wob, oracle, dtype, g, variant):
+    torch = torch_mod()
+    N, K = 64, 512
+    d = wl.w4a16_inputs(1, N, K, g, dtype, seed=g + dtype, symmetric=(variant == "sym"),
+                        signed_scales=(variant == "signed"))
+    t = w4a16_to_device(d)
+    w32_ref = oracle.w4a16_dequant(d["qweight"], d["scales"], dtype, d["qzeros"], N, K, g)
+    w32 = wob.w4a16_dequant(t["qweight"], t["scales"], t["qzeros"], g).cpu().numpy()
+    assert np.array_equal(w32.view(np.uint32), w32_ref.view(np.uint32))
+    wa_ref = oracle.w4a16_dequant_act(d["qweight"], d["scales"], dtype, d["qzeros"], N, K, g)
+    wa = host_bits(wob.w4a16_dequant(t["qweight"], t["scales"], t["qzeros"], g,
+                                     out_dtype=t["scales"].dtype))
+    assert np.array_equal(wa, wa_ref)
+
+
+def test_mxfp4_dequant_probe_bit_exact(wob, oracle):
+    torch = torch_mod()
+    rng = np.random.default_rng(0)
+    N, K = 32, 256
+    codes = rng.integers(0, 16, (N, K))
+    codes[0, :16] = np.arange(16)  # every code once, in order
+    w_fp4 = wl.pack_fp4_pairs(codes)
+    w_scale = rng.integers(118, 127, (N, K // 32)).astype(np.uint8)
+    w_scale[0, 0] = 127
+    ref = oracle.mxfp4_dequant(w_fp4, w_scale, N, K).astype(np.float64)
+    out = wob.mxfp4_dequant(dev(w_fp4), dev(w_scale))
+    got = oracle.bf16_decode(host_bits(out))
+    assert np.array_equal(got, ref), (got[0, :16], ref[0, :16])

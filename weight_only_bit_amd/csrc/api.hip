@@ -1,0 +1,282 @@
+// C-ABI layer: argument validation, architecture gate and kernel dispatch for
+// the entry points declared in include/weight_only_bit.h.  Every check runs
+// before any device call, so a non-OK status means nothing was enqueued.
+#include "weight_only_bit.h"
+#include "wob_device.hpp"
+#include "wob_internal.hpp"
+
+#include <limits.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok()
+{
+    g_last_error[0] = 0;
+    return WOB_OK;
+}
+
+// Per-device cache of the architecture check: 0 unknown, 1 gfx950, 2 other.
+int g_arch[64];
+
+int arch_gate()
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(WOB_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64)
+        return fail(WOB_UNSUPPORTED, "device ordinal %d out of range", dev);
+    if (g_arch[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(WOB_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        g_arch[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    if (g_arch[dev] != 1)
+        return fail(WOB_UNSUPPORTED, "device %d is not gfx950", dev);
+    return WOB_OK;
+}
+
+int launched(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(WOB_HIP, "%s launch: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared W4A16 operand checks.  M may be 0 (no-op) for the dense form.
+int check_w4(const void *x, int x_dtype, const int32_t *qweight, const void *scales,
+             int scales_dtype, const void *qzeros, int zeros_dtype, const void *y, int64_t M,
+             int64_t N, int64_t K, int64_t g)
+{
+    if (x_dtype != WOB_F16 && x_dtype != WOB_BF16)
+        return fail(WOB_DTYPE, "x dtype tag %d is not F16 or BF16", x_dtype);
+    if (scales_dtype != x_dtype)
+        return fail(WOB_DTYPE, "scales dtype tag %d differs from x dtype tag %d", scales_dtype,
+                    x_dtype);
+    if (qzeros && zeros_dtype != WOB_U4X8_I32)
+        return fail(WOB_DTYPE,
+                    "zero-points must be packed 4-bit (U4X8_I32); dtype tag %d is refused",
+                    zeros_dtype);
+    if (M < 0 || N < 0 || K < 32)
+        return fail(WOB_INVALID_ARG, "bad shape M=%lld N=%lld K=%lld", (long long)M, (long long)N,
+                    (long long)K);
+    if (g != 32 && g != 64 && g != 128)
+        return fail(WOB_UNSUPPORTED, "group size %lld is not 32, 64 or 128", (long long)g);
+    if (K % g != 0 || K % 32 != 0)
+        return fail(WOB_INVALID_ARG, "K=%lld is not a multiple of the group size %lld and of 32",
+                    (long long)K, (long long)g);
+    if (N % 8 != 0)
+        return fail(WOB_INVALID_ARG, "N=%lld is not a multiple of 8", (long long)N);
+    if (M > INT_MAX / 2 || N > INT_MAX / 2 || K > INT_MAX / 2 || (N / 8) * K > (int64_t)INT_MAX * 8)
+        return fail(WOB_INVALID_ARG, "shape too large");
+    if (M == 0 || N == 0)
+        return WOB_OK;
+    if (!x || !qweight || !scales || !y)
+        return fail(WOB_INVALID_ARG, "null operand pointer");
+    if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y) ||
+        (qzeros && !aligned16(qzeros)))
+        return fail(WOB_INVALID_ARG, "operand pointers must be 16-byte aligned");
+    return WOB_OK;
+}
+
+wob::W4Args make_args(const void *x, int dt, const int32_t *qweight, const void *scales,
+                      const void *qzeros, void *y, int64_t M, int64_t N, int64_t K, int64_t g)
+{
+    wob::W4Args a;
+    a.x = x;
+    a.qweight = reinterpret_cast<const uint32_t *>(qweight);
+    a.scales = scales;
+    a.qzeros = static_cast<const uint32_t *>(qzeros);
+    a.y = y;
+    a.dt = dt == WOB_F16 ? wob::DT_F16 : wob::DT_BF16;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.g = (int)g;
+    return a;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *wob_status_str(int status)
+{
+    switch (status) {
+    case WOB_OK: return "ok";
+    case WOB_INVALID_ARG: return "invalid argument";
+    case WOB_DTYPE: return "unsupported dtype for this operand";
+    case WOB_UNSUPPORTED: return "unsupported device or parameter";
+    case WOB_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *wob_last_error(void) { return g_last_error; }
+
+int wob_device_check(void)
+{
+    int s = arch_gate();
+    return s == WOB_OK ? ok() : s;
+}
+
+int w4a16_gemm_ex(const void *x, int x_dtype, const int32_t *qweight, const void *scales,
+                  int scales_dtype, const void *qzeros, int zeros_dtype, void *y, int64_t M,
+                  int64_t N, int64_t K, int64_t group_size, int path, void *stream)
+{
+    int s = check_w4(x, x_dtype, qweight, scales, scales_dtype, qzeros, zeros_dtype, y, M, N, K,
+                     group_size);
+    if (s != WOB_OK)
+        return s;
+    if (path != WOB_PATH_AUTO && path != WOB_PATH_SKINNY && path != WOB_PATH_TILED)
+        return fail(WOB_INVALID_ARG, "unknown path %d", path);
+    if (path == WOB_PATH_SKINNY && !wob::skinny_fits((int)(M ? M : 1), (int)(N ? N : 8), (int)K, (int)group_size))
+        return fail(WOB_INVALID_ARG, "skinny path needs M <= 8 and M*K small enough for LDS");
+    if (M == 0 || N == 0)
+        return ok();
+    s = arch_gate();
+    if (s != WOB_OK)
+        return s;
+    wob::W4Args a = make_args(x, x_dtype, qweight, scales, qzeros, y, M, N, K, group_size);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool skinny = path == WOB_PATH_SKINNY || (path == WOB_PATH_AUTO && wob::skinny_fits(a.M, a.N, a.K, a.g));
+    if (skinny)
+        return launched(wob::launch_w4a16_skinny(a, st), "w4a16 skinny");
+    return launched(wob::launch_w4a16_tiled(a, st), "w4a16 tiled");
+}
+
+int w4a16_gemm(const void *x, int x_dtype, const int32_t *qweight, const void *scales,
+               int scales_dtype, const void *qzeros, int zeros_dtype, void *y, int64_t M,
+               int64_t N, int64_t K, int64_t group_size, void *stream)
+{
+    return w4a16_gemm_ex(x, x_dtype, qweight, scales, scales_dtype, qzeros, zeros_dtype, y, M, N,
+                         K, group_size, WOB_PATH_AUTO, stream);
+}
+
+int w4a16_gemm_grouped(const void *x, int x_dtype, const int64_t *m_offsets, int64_t num_groups,
+                       int64_t total_M, const int32_t *qweight, const void *scales,
+                       int scales_dtype, const void *qzeros, int zeros_dtype, void *y, int64_t N,
+                       int64_t K, int64_t group_size, void *stream)
+{
+    int s = check_w4(x, x_dtype, qweight, scales, scales_dtype, qzeros, zeros_dtype, y, total_M,
+                     N, K, group_size);
+    if (s != WOB_OK)
+        return s;
+    if (num_groups < 0 || num_groups > 65535)
+        return fail(WOB_INVALID_ARG, "num_groups=%lld outside [0, 65535]", (long long)num_groups);
+    if (total_M == 0 || N == 0 || num_groups == 0)
+        return ok();
+    if (!m_offsets || !aligned16(m_offsets))
+        return fail(WOB_INVALID_ARG, "m_offsets must be a 16-byte aligned device pointer");
+    s = arch_gate();
+    if (s != WOB_OK)
+        return s;
+    wob::W4Args a = make_args(x, x_dtype, qweight, scales, qzeros, y, total_M, N, K, group_size);
+    return launched(wob::launch_w4a16_grouped(a, m_offsets, (int)num_groups,
+                                              static_cast<hipStream_t>(stream)),
+                    "w4a16 grouped");
+}
+
+size_t mxfp4_moe_gemm_workspace_size(int64_t T, int64_t topk, int64_t E)
+{
+    if (T < 0 || topk < 1 || E < 1)
+        return 0;
+    return wob::moe_workspace_bytes(T, topk, E);
+}
+
+int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
+                   const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E, int64_t N,
+                   int64_t K, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (T < 0 || topk < 1 || E < 1 || N < 0 || K < 32)
+        return fail(WOB_INVALID_ARG, "bad shape T=%lld topk=%lld E=%lld N=%lld K=%lld",
+                    (long long)T, (long long)topk, (long long)E, (long long)N, (long long)K);
+    if (K % 32 != 0 || N % 16 != 0)
+        return fail(WOB_INVALID_ARG, "need K %% 32 == 0 and N %% 16 == 0 (K=%lld N=%lld)",
+                    (long long)K, (long long)N);
+    if (T > INT_MAX / 64 || topk > 64 || E > 4096 || N > INT_MAX / 2 || K > INT_MAX / 2 ||
+        E * N * (K / 2) > ((int64_t)1 << 40))
+        return fail(WOB_INVALID_ARG, "shape too large");
+    if (T == 0 || N == 0)
+        return ok();
+    if (!x || !topk_ids || !w_fp4 || !w_scale || !y)
+        return fail(WOB_INVALID_ARG, "null operand pointer");
+    if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(w_fp4) || !aligned16(w_scale) ||
+        !aligned16(y))
+        return fail(WOB_INVALID_ARG, "operand pointers must be 16-byte aligned");
+    const size_t need = wob::moe_workspace_bytes(T, topk, E);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+        return fail(WOB_INVALID_ARG, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    int s = arch_gate();
+    if (s != WOB_OK)
+        return s;
+    return launched(wob::launch_mxfp4_moe(x, topk_ids, w_fp4, w_scale, y, (int)T, (int)topk,
+                                          (int)E, (int)N, (int)K, workspace,
+                                          static_cast<hipStream_t>(stream)),
+                    "mxfp4 moe");
+}
+
+int w4a16_dequant(const int32_t *qweight, const void *scales, int scales_dtype,
+                  const void *qzeros, int zeros_dtype, void *out, int out_dtype, int64_t N,
+                  int64_t K, int64_t group_size, void *stream)
+{
+    // x is not an operand of the probe; validate the weights as for a GEMM.
+    int s = check_w4(qweight, scales_dtype, qweight, scales, scales_dtype, qzeros, zeros_dtype,
+                     out, 1, N, K, group_size);
+    if (s != WOB_OK)
+        return s;
+    if (out_dtype != WOB_F32 && out_dtype != scales_dtype)
+        return fail(WOB_DTYPE, "probe output dtype %d must be F32 or the scales dtype", out_dtype);
+    if (N == 0)
+        return ok();
+    s = arch_gate();
+    if (s != WOB_OK)
+        return s;
+    return launched(wob::launch_w4a16_dequant(reinterpret_cast<const uint32_t *>(qweight), scales,
+                                              static_cast<const uint32_t *>(qzeros), out,
+                                              scales_dtype == WOB_F16 ? wob::DT_F16 : wob::DT_BF16,
+                                              out_dtype == WOB_F32, (int)N, (int)K,
+                                              (int)group_size, static_cast<hipStream_t>(stream)),
+                    "w4a16 dequant probe");
+}
+
+int mxfp4_dequant(const uint8_t *w_fp4, const uint8_t *w_scale, void *out, int64_t N, int64_t K,
+                  void *stream)
+{
+    if (N < 0 || K < 32 || K % 32 != 0 || N > INT_MAX / 2 || K > INT_MAX / 2)
+        return fail(WOB_INVALID_ARG, "bad shape N=%lld K=%lld", (long long)N, (long long)K);
+    if (N == 0)
+        return ok();
+    if (!w_fp4 || !w_scale || !out)
+        return fail(WOB_INVALID_ARG, "null operand pointer");
+    if (!aligned16(w_fp4) || !aligned16(out))
+        return fail(WOB_INVALID_ARG, "operand pointers must be 16-byte aligned");
+    int s = arch_gate();
+    if (s != WOB_OK)
+        return s;
+    return launched(wob::launch_mxfp4_dequant(w_fp4, w_scale, out, (int)N, (int)K,
+                                              static_cast<hipStream_t>(stream)),
+                    "mxfp4 dequant probe");
+}
+
+} // extern "C"

@@ -1,0 +1,467 @@
+// Skinny W4A16 GEMV for M <= 8 (decode and small batch) on gfx950.
+//
+// The zero-point page ("Keep W4A16 zero-points packed at 4 bits instead of
+// expanding to 2 bytes", sections Problem and Known regression) establishes
+// that this kernel sits at the memory roofline: its time follows the bytes it
+// streams (packed codes, scales and packed zero-points), and at batch 4 with
+// g = 128 the nibble extraction shows up as compute when loads and math do not
+// overlap.  The design below therefore
+//   * reads every weight byte exactly once with 16-byte coalesced loads,
+//   * issues a batch of U independent loads per lane before any math on them,
+//     so U * 16 bytes per lane stay in flight,
+//   * keeps the zero-points packed and extracts the nibble in registers,
+//   * spends about two vector ALU operations per weight (packed binary16 or
+//     bfloat16 dot products on unpacked pairs).
+//
+// Work decomposition.  A wavefront owns RO row octets (an octet is 8
+// consecutive rows, the rows that share one packed zero-point word) and one
+// contiguous range of 32-value K chunks; `ksplit` waves of a workgroup split K
+// for the same octets.  Lane (r, q) = (lane/8, lane%8) handles row r of each of
+// its octets and the chunks c0 + q + 8*i of its range, so each load
+// instruction covers eight 128-byte row segments, and the activations of a
+// chunk are read from LDS once for all RO rows of the lane.  One chunk is one 16-byte load (four words, 32 codes) and
+// lies inside a single quantization group for every g in {32, 64, 128}.
+//
+// Prologue.  The workgroup stages X (in word order, see wob_device.hpp), the
+// chunk sums of X, and the scales and packed zero-point words of its rows in
+// LDS with a few coalesced 16-byte loads per thread.  Each wave issues its
+// first batch of weight loads before it waits for the staging loads, so the
+// prologue latency hides behind weight traffic.  The per-chunk metadata then
+// costs two LDS reads instead of two small global loads.
+//
+// Arithmetic: each word is unpacked with byte permutes into four pairs of
+// biased 16-bit numbers (B + q), B = 1024 for binary16 and 128 for bfloat16,
+// which are exact, and fed to v_dot2_f32_f16 / v_dot2_f32_bf16 with the
+// activation pairs.  Per chunk, sum_k (q_k - z) x_k = sum_k (B + q_k) x_k -
+// (B + z) * sum_k x_k; the chunk result is scaled once.  Products are exact in
+// fp32 and accumulation is fp32; the bias term adds a rounding error of order
+// 2^-24 * B * sum|x| per chunk, far inside the parity tolerance.  About 1.5
+// vector operations per weight at M = 1.
+//
+// Weight loads stream through a ring of D chunk slots: computing chunk i frees
+// its slot, which immediately receives the load of chunk i + D.  One load is
+// issued per chunk computed, so each wave's requests stay smooth instead of
+// bursty (measured: batches of several chunks per issue point run slower),
+// and D - 1 chunks per row stay in flight while a chunk is computed.
+// Partial sums are reduced over the 8 lanes of a row with cross-lane moves
+// and, for ksplit > 1, over waves through LDS.
+#include "wob_device.hpp"
+#include "wob_internal.hpp"
+
+namespace wob {
+namespace {
+
+constexpr int SK_WAVES = 4;
+constexpr int SK_THREADS = 64 * SK_WAVES;
+constexpr int SK_LDS_BUDGET = 64 * 1024;
+constexpr int SK_RING = 3; // chunk slots per row in the load ring
+
+// Prologue register budget: loads per thread issued before the first wait.
+constexpr int SK_XR = 4; // X blocks (covers M*K <= 8192)
+constexpr int SK_SR = 3; // 16-byte scale blocks
+constexpr int SK_ZR = 3; // zero-point words
+
+// LDS carve-up, in bytes, shared by the kernel and the host-side size check.
+struct SkLds {
+    int x, xsum, sc, zp, red, total;
+    __host__ __device__ SkLds(int M, int K, int G, int octs_per_wg)
+    {
+        const int RB = ((K + 255) >> 8) * 32; // 16-byte blocks per X row
+        x = 0;
+        xsum = x + M * RB * 16;
+        sc = xsum + M * (K >> 5) * 4;
+        zp = sc + ((octs_per_wg * 8 * G * 2 + 15) & ~15);
+        red = zp + ((octs_per_wg * G * 4 + 15) & ~15);
+        total = red + SK_WAVES * 2 * M * 8 * 4; // up to two octets per wave
+    }
+};
+
+// Occupancy target per SIMD: enough resident waves for one wave generation on
+// the decode shapes (fewer for the register-heavy larger M).
+template <int M, int RO>
+constexpr int sk_min_waves() { return RO == 2 ? 3 : (M <= 2 ? 4 : 2); }
+
+template <int DT, int M, int D, int GS, bool HAS_Z, int RO>
+__global__ __launch_bounds__(SK_THREADS, (sk_min_waves<M, RO>())) void w4a16_skinny_kernel(
+    const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
+    const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros,
+    uint16_t *__restrict__ y, int N, int K, int ksplit)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int C = K >> 5;  // chunks per row
+    const int G = C >> GS; // groups per row
+    const int RB = ((K + 255) >> 8) * 32;
+    const int NO = N >> 3; // row octets
+    const int octs_per_wg = SK_WAVES / ksplit * RO;
+    const SkLds L(M, K, G, octs_per_wg);
+    u32x4 *xl = reinterpret_cast<u32x4 *>(smem + L.x);
+    float *xsum = reinterpret_cast<float *>(smem + L.xsum);
+    uint16_t *sl = reinterpret_cast<uint16_t *>(smem + L.sc);
+    uint32_t *zl = reinterpret_cast<uint32_t *>(smem + L.zp);
+    float *red = reinterpret_cast<float *>(smem + L.red);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int oct0 = blockIdx.x * octs_per_wg;
+    const int nocts = min(octs_per_wg, NO - oct0);
+
+    // ---- prologue loads: X, scales, zero-points (unconditional, clamped) ----
+    const u32x4 *xs = reinterpret_cast<const u32x4 *>(x);
+    const int nvec = (M * K) >> 3;
+    u32x4 xr[SK_XR];
+#pragma unroll
+    for (int t = 0; t < SK_XR; ++t)
+        xr[t] = xs[min(tid + SK_THREADS * t, nvec - 1)];
+    const u32x4 *ss = reinterpret_cast<const u32x4 *>(scales + (size_t)oct0 * 8 * G);
+    const int nsb = nocts * G; // 16-byte blocks of this workgroup's scales
+    u32x4 sr[SK_SR];
+#pragma unroll
+    for (int t = 0; t < SK_SR; ++t)
+        sr[t] = ss[min(tid + SK_THREADS * t, nsb - 1)];
+    const uint32_t *zs = HAS_Z ? qzeros + (size_t)oct0 * G : nullptr;
+    const int nzw = nocts * G;
+    uint32_t zr[SK_ZR];
+    if constexpr (HAS_Z) {
+#pragma unroll
+        for (int t = 0; t < SK_ZR; ++t)
+            zr[t] = zs[min(tid + SK_THREADS * t, nzw - 1)];
+    }
+
+    // ---- this wave's work ----
+    const int woct = (wave / ksplit) * RO; // first octet of this wave within the workgroup
+    const int oct = oct0 + woct;
+    const int ks = wave % ksplit;
+    const int r = lane >> 3;
+    const int q = lane & 7;
+    const int cper = ((C + ksplit - 1) / ksplit + 7) & ~7;
+    const int c0 = ks * cper;
+    const int c1 = min(C, c0 + cper);
+    const int jf = c0 + q; // this lane's first chunk
+    const int n_it = (oct < NO && jf < c1) ? (c1 - jf + 7) >> 3 : 0;
+    const int jfc = min(jf, C - 1);
+    const u32x4 *wp[RO]; // row r of each octet (clamped into the matrix)
+#pragma unroll
+    for (int o = 0; o < RO; ++o)
+        wp[o] = reinterpret_cast<const u32x4 *>(qweight +
+                                                (size_t)(min(oct + o, NO - 1) * 8 + r) * (K >> 3)) +
+                jfc;
+
+    // Fill the ring with chunks 0..D-1 before any wait (clamped into the row).
+    u32x4 ring[D][RO];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+#pragma unroll
+        for (int o = 0; o < RO; ++o)
+            ring[d][o] = __builtin_nontemporal_load(wp[o] + 8 * min(d, max(n_it - 1, 0)));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- stage X (word order, conflict-free block layout) and chunk sums ----
+    const int rowblk = K >> 3;
+#pragma unroll
+    for (int t = 0; t < SK_XR; ++t) {
+        const int i = tid + SK_THREADS * t;
+        float bs = 0.f; // sum of this block's 8 values
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (DT == DT_F16)
+                bs = __builtin_amdgcn_fdot2(bitcast<half2_t>(xr[t][e]),
+                                            half2_t{(_Float16)1.f, (_Float16)1.f}, bs, false);
+            else
+                bs = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(xr[t][e]),
+                                                     bitcast<bf162_t>(0x3F803F80u), bs, false);
+        }
+        // the four blocks of a chunk sit in four consecutive lanes
+        bs += __shfl_xor(bs, 1);
+        bs += __shfl_xor(bs, 2);
+        if (i < nvec) {
+            const int m = i / rowblk;
+            const int tb = i - m * rowblk;
+            const int j = tb >> 2, wi = tb & 3;
+            xl[m * RB + (j >> 3) * 32 + wi * 8 + (j & 7)] = to_word_order(xr[t]);
+            if (wi == 0)
+                xsum[m * C + j] = bs;
+        }
+    }
+    {
+        u32x4 *sd = reinterpret_cast<u32x4 *>(sl);
+#pragma unroll
+        for (int t = 0; t < SK_SR; ++t) {
+            const int i = tid + SK_THREADS * t;
+            if (i < nsb)
+                sd[i] = sr[t];
+        }
+        if constexpr (HAS_Z) {
+#pragma unroll
+            for (int t = 0; t < SK_ZR; ++t) {
+                const int i = tid + SK_THREADS * t;
+                if (i < nzw)
+                    zl[i] = zr[t];
+            }
+        }
+    }
+    // Rare large shapes: whatever did not fit the prologue registers.
+    for (int i = tid + SK_THREADS * SK_XR; i < nvec; i += SK_THREADS) {
+        const u32x4 v = xs[i];
+        float bs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (DT == DT_F16)
+                bs = __builtin_amdgcn_fdot2(bitcast<half2_t>(v[e]),
+                                            half2_t{(_Float16)1.f, (_Float16)1.f}, bs, false);
+            else
+                bs = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(v[e]),
+                                                     bitcast<bf162_t>(0x3F803F80u), bs, false);
+        }
+        bs += __shfl_xor(bs, 1);
+        bs += __shfl_xor(bs, 2);
+        const int m = i / rowblk;
+        const int tb = i - m * rowblk;
+        const int j = tb >> 2, wi = tb & 3;
+        xl[m * RB + (j >> 3) * 32 + wi * 8 + (j & 7)] = to_word_order(v);
+        if (wi == 0)
+            xsum[m * C + j] = bs;
+    }
+    for (int i = tid + SK_THREADS * SK_SR; i < nsb; i += SK_THREADS)
+        reinterpret_cast<u32x4 *>(sl)[i] = ss[i];
+    if constexpr (HAS_Z) {
+        for (int i = tid + SK_THREADS * SK_ZR; i < nzw; i += SK_THREADS)
+            zl[i] = zs[i];
+    }
+    __syncthreads();
+
+    constexpr uint32_t MAGIC = DT == DT_F16 ? MAGIC4_F16 : MAGIC4_BF16;
+    constexpr float BIAS = DT == DT_F16 ? 1024.f : 128.f;
+    constexpr int SU = 8 >> GS; // scale / zero-point index step per chunk step of 8
+
+    float acc[RO][M];
+#pragma unroll
+    for (int o = 0; o < RO; ++o)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            acc[o][m] = 0.f;
+    // octets of this wave that exist (the last workgroup may be partial)
+    const int ro_valid = min(RO, NO - oct);
+
+    if (n_it > 0) {
+        // this lane's LDS data: X blocks of chunk jf + 8 i, word wi at 32 i + 8 wi
+        const u32x4 *xb0 = xl + (jf >> 3) * 32 + (jf & 7);
+        const float *xs0 = xsum + jf;
+        const uint16_t *sp = sl + (woct * 8 + r) * G + (jf >> GS); // octet o: + 8 G o
+        const uint32_t *zp = zl + woct * G + (jf >> GS);            // octet o: + G o
+
+        auto chunk = [&](int i, const u32x4(&wv)[RO]) {
+            // unpack every row's word pairs first; then, per activation row,
+            // read that row's X blocks once and use them for all RO rows
+            u32x4 pr[RO][4];
+            float sc[RO], bias[RO];
+#pragma unroll
+            for (int o = 0; o < RO; ++o) {
+                sc[o] = act_to_f32<DT>(sp[8 * G * o + SU * i]);
+                const uint32_t z = HAS_Z ? nib(zp[G * o + SU * i], r) : 8u;
+                bias[o] = BIAS + (float)z;
+#pragma unroll
+                for (int wi = 0; wi < 4; ++wi)
+                    pr[o][wi] = nib_pairs_biased(wv[o][wi], MAGIC);
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                u32x4 xv[4];
+#pragma unroll
+                for (int wi = 0; wi < 4; ++wi)
+                    xv[wi] = xb0[m * RB + 32 * i + 8 * wi];
+                const float xsv = xs0[m * C + 8 * i];
+#pragma unroll
+                for (int o = 0; o < RO; ++o) {
+                    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                    for (int wi = 0; wi < 4; ++wi) {
+                        const u32x4 x4 = xv[wi];
+                        if constexpr (DT == DT_F16) {
+                            a0 = __builtin_amdgcn_fdot2(bitcast<half2_t>(pr[o][wi][0]), bitcast<half2_t>(x4[0]), a0, false);
+                            a1 = __builtin_amdgcn_fdot2(bitcast<half2_t>(pr[o][wi][1]), bitcast<half2_t>(x4[1]), a1, false);
+                            a0 = __builtin_amdgcn_fdot2(bitcast<half2_t>(pr[o][wi][2]), bitcast<half2_t>(x4[2]), a0, false);
+                            a1 = __builtin_amdgcn_fdot2(bitcast<half2_t>(pr[o][wi][3]), bitcast<half2_t>(x4[3]), a1, false);
+                        } else {
+                            a0 = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(pr[o][wi][0]), bitcast<bf162_t>(x4[0]), a0, false);
+                            a1 = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(pr[o][wi][1]), bitcast<bf162_t>(x4[1]), a1, false);
+                            a0 = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(pr[o][wi][2]), bitcast<bf162_t>(x4[2]), a0, false);
+                            a1 = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(pr[o][wi][3]), bitcast<bf162_t>(x4[3]), a1, false);
+                        }
+                    }
+                    const float t = fmaf(-bias[o], xsv, a0 + a1);
+                    acc[o][m] = fmaf(sc[o], t, acc[o][m]);
+                }
+            }
+        };
+        // Steady state: compute chunk i + d from slot d, then refill the slot
+        // with chunk i + d + D.  Loads here are unconditional so the wait
+        // counts stay exact; the scheduling barriers keep the compiler from
+        // moving a refill across the computation it should overlap.
+        int i = 0;
+        for (; i + 2 * D <= n_it; i += D) {
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                chunk(i + d, ring[d]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int o = 0; o < RO; ++o)
+                    ring[d][o] = __builtin_nontemporal_load(wp[o] + 8 * (i + d + D));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // Drain: the ring holds chunks i .. i+D-1 (those below n_it); the
+        // fewer than D chunks after them are loaded one at a time.
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (i + d < n_it)
+                chunk(i + d, ring[d]);
+        for (int j = i + D; j < n_it; ++j) {
+            u32x4 w1[RO];
+#pragma unroll
+            for (int o = 0; o < RO; ++o)
+                w1[o] = __builtin_nontemporal_load(wp[o] + 8 * j);
+            chunk(j, w1);
+        }
+    }
+
+    // Reduce over the 8 lanes of a row.
+#pragma unroll
+    for (int o = 0; o < RO; ++o)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float v = acc[o][m];
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 4);
+            acc[o][m] = v;
+        }
+
+    if (ksplit == 1) {
+        if (q == 0) {
+#pragma unroll
+            for (int o = 0; o < RO; ++o) {
+                if (o >= ro_valid)
+                    break;
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    y[(size_t)m * N + (oct + o) * 8 + r] = f32_to_act<DT>(acc[o][m]);
+            }
+        }
+        return;
+    }
+    if (q == 0) {
+#pragma unroll
+        for (int o = 0; o < RO; ++o)
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                red[((wave * RO + o) * M + m) * 8 + r] = acc[o][m];
+    }
+    __syncthreads();
+    if (ks == 0 && q == 0) {
+#pragma unroll
+        for (int o = 0; o < RO; ++o) {
+            if (o >= ro_valid)
+                break;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float v = 0.f;
+                for (int w = 0; w < ksplit; ++w)
+                    v += red[(((wave + w) * RO + o) * M + m) * 8 + r];
+                y[(size_t)m * N + (oct + o) * 8 + r] = f32_to_act<DT>(v);
+            }
+        }
+    }
+}
+
+// Octets per wave: two when there are enough rows to keep every CU busy.
+int ro_for(int M, int N) { return (M <= 2 && N / 8 >= 4096) ? 2 : 1; }
+
+int ksplit_for(int N, int K)
+{
+    // Split K across waves of a workgroup while there are few row octets,
+    // keeping at least two chunks per lane.
+    const int octs = N / 8;
+    const int C = K / 32;
+    int ksplit = 1;
+    while (ksplit < SK_WAVES && octs * ksplit < 4096 && C >= 16 * ksplit * 2)
+        ksplit *= 2;
+    return ksplit;
+}
+
+int lds_bytes(int M, int N, int K, int g)
+{
+    return SkLds(M, K, K / g, SK_WAVES / ksplit_for(N, K) * ro_for(M, N)).total;
+}
+
+template <int DT, int M, int GS, int RO>
+hipError_t launch_r(const W4Args &a, int grid, int ksplit, size_t lds, hipStream_t stream)
+{
+    if (a.qzeros)
+        hipLaunchKernelGGL((w4a16_skinny_kernel<DT, M, SK_RING, GS, true, RO>), dim3(grid),
+                           dim3(SK_THREADS), lds, stream, static_cast<const uint16_t *>(a.x),
+                           a.qweight, static_cast<const uint16_t *>(a.scales), a.qzeros,
+                           static_cast<uint16_t *>(a.y), a.N, a.K, ksplit);
+    else
+        hipLaunchKernelGGL((w4a16_skinny_kernel<DT, M, SK_RING, GS, false, RO>), dim3(grid),
+                           dim3(SK_THREADS), lds, stream, static_cast<const uint16_t *>(a.x),
+                           a.qweight, static_cast<const uint16_t *>(a.scales), a.qzeros,
+                           static_cast<uint16_t *>(a.y), a.N, a.K, ksplit);
+    return hipGetLastError();
+}
+
+template <int DT, int M, int GS>
+hipError_t launch_g(const W4Args &a, int grid, int ksplit, size_t lds, hipStream_t stream)
+{
+    if constexpr (M <= 2) {
+        if (ro_for(M, a.N) == 2)
+            return launch_r<DT, M, GS, 2>(a, grid, ksplit, lds, stream);
+    }
+    return launch_r<DT, M, GS, 1>(a, grid, ksplit, lds, stream);
+}
+
+template <int DT, int M>
+hipError_t launch_m(const W4Args &a, hipStream_t stream)
+{
+    const int ksplit = ksplit_for(a.N, a.K);
+    const int octs_per_wg = SK_WAVES / ksplit * ro_for(M, a.N);
+    const int grid = (a.N / 8 + octs_per_wg - 1) / octs_per_wg;
+    const size_t lds = (size_t)lds_bytes(M, a.N, a.K, a.g);
+    switch (a.g) {
+    case 32: return launch_g<DT, M, 0>(a, grid, ksplit, lds, stream);
+    case 64: return launch_g<DT, M, 1>(a, grid, ksplit, lds, stream);
+    default: return launch_g<DT, M, 2>(a, grid, ksplit, lds, stream);
+    }
+}
+
+template <int DT>
+hipError_t launch_dt(const W4Args &a, hipStream_t stream)
+{
+    switch (a.M) {
+    case 1: return launch_m<DT, 1>(a, stream);
+    case 2: return launch_m<DT, 2>(a, stream);
+    case 3: return launch_m<DT, 3>(a, stream);
+    case 4: return launch_m<DT, 4>(a, stream);
+    case 5: return launch_m<DT, 5>(a, stream);
+    case 6: return launch_m<DT, 6>(a, stream);
+    case 7: return launch_m<DT, 7>(a, stream);
+    case 8: return launch_m<DT, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+} // namespace
+
+bool skinny_fits(int M, int N, int K, int g)
+{
+    return M >= 1 && M <= 8 && lds_bytes(M, N, K, g) <= SK_LDS_BUDGET;
+}
+
+hipError_t launch_w4a16_skinny(const W4Args &a, hipStream_t stream)
+{
+    if (!skinny_fits(a.M, a.N, a.K, a.g))
+        return hipErrorInvalidValue;
+    return a.dt == DT_F16 ? launch_dt<DT_F16>(a, stream) : launch_dt<DT_BF16>(a, stream);
+}
+
+} // namespace wob

@@ -1,0 +1,184 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, bit casts,
+// the 4-bit unpack/dequantize primitives and activation conversions.
+//
+// Nibble layout (zero-point page "Keep W4A16 zero-points packed at 4 bits
+// instead of expanding to 2 bytes", section Change; the weight words use the
+// same rule along K): value i of a packed word sits in bits 4*i.
+//
+// Element order inside a word.  Shifting a word right by 4p and masking with
+// 0x000F000F leaves value p in the low half and value p+4 in the high half.
+// OR-ing 0x6400 (binary16 1024.0) into each half turns them into the exact
+// binary16 numbers 1024+q, and subtracting 1024+z gives q-z exactly.  A word
+// therefore dequantizes into four half pairs holding values
+//     (0,4) (1,5) (2,6) (3,7)
+// so every consumer stores the matching activations in that same order
+// ("word order" below).  A dot product is invariant under a common
+// permutation of both operands, so the order never changes a result.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wob {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From &f)
+{
+    static_assert(sizeof(To) == sizeof(From), "bitcast size");
+    return __builtin_bit_cast(To, f);
+}
+
+// Word-order position p (0..7) holds value perm(p) of a packed word.
+__host__ __device__ constexpr int word_order_value(int p) { return (p >> 1) + 4 * (p & 1); }
+
+// Re-order eight consecutive 16-bit activations (natural order, four dwords)
+// into word order: out dword j = (value j, value j+4).
+__device__ __forceinline__ u32x4 to_word_order(u32x4 v)
+{
+    u32x4 o;
+    // v_perm_b32 selector: bytes 0-3 come from src1, 4-7 from src0.
+    o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u); // lo(v.x) | lo(v.z) << 16
+    o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u); // hi(v.x) | hi(v.z) << 16
+    o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+    o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+    return o;
+}
+
+// ---------------------------------------------------------------------------
+// 4-bit unpack
+// ---------------------------------------------------------------------------
+
+// High byte of the biased 16-bit numbers: 0x64 gives binary16 1024 + q,
+// 0x43 gives bfloat16 128 + q (q < 16 sits in the low mantissa bits).
+constexpr uint32_t MAGIC4_F16 = 0x64646464u;
+constexpr uint32_t MAGIC4_BF16 = 0x43434343u;
+
+// All four biased pairs of a word, in word order, with byte permutes: after
+// masking, the even values sit in the bytes of t0 and the odd ones in t1, and
+// v_perm_b32 interleaves two of those bytes with two magic bytes.  Seven
+// vector operations per word.
+__device__ __forceinline__ u32x4 nib_pairs_biased(uint32_t w, uint32_t magic4)
+{
+    const uint32_t t0 = w & 0x0F0F0F0Fu;        // values 0, 2, 4, 6 in bytes 0..3
+    const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu; // values 1, 3, 5, 7
+    u32x4 o;
+    // selector bytes 0-3 pick from t (src1), 4 picks the magic byte (src0)
+    o[0] = __builtin_amdgcn_perm(magic4, t0, 0x04020400u); // (v0, v4)
+    o[1] = __builtin_amdgcn_perm(magic4, t1, 0x04020400u); // (v1, v5)
+    o[2] = __builtin_amdgcn_perm(magic4, t0, 0x04030401u); // (v2, v6)
+    o[3] = __builtin_amdgcn_perm(magic4, t1, 0x04030401u); // (v3, v7)
+    return o;
+}
+
+// Zero-point of row r (0..7) in a packed zero-point word.
+__device__ __forceinline__ uint32_t nib(uint32_t w, int r) { return (w >> (4 * r)) & 0xFu; }
+
+// binary16 pair (-(1024+z), -(1024+z)): adding it to a biased pair gives q - z.
+__device__ __forceinline__ half2_t f16_neg_bias(uint32_t z)
+{
+    return bitcast<half2_t>((0xE400u | z) * 0x00010001u);
+}
+
+// ---------------------------------------------------------------------------
+// Activation conversions
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float act_to_f32(uint16_t v, int dt)
+{
+    if (dt == DT_F16)
+        return (float)bitcast<_Float16>(v);
+    return bitcast<float>((uint32_t)v << 16);
+}
+
+template <int DT>
+__device__ __forceinline__ float act_to_f32(uint16_t v)
+{
+    if constexpr (DT == DT_F16)
+        return (float)bitcast<_Float16>(v);
+    else
+        return bitcast<float>((uint32_t)v << 16);
+}
+
+// fp32 -> activation dtype, round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint16_t f32_to_act(float f)
+{
+    if constexpr (DT == DT_F16)
+        return bitcast<uint16_t>((_Float16)f);
+    else
+        return bitcast<uint16_t>((__bf16)f);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t f32x2_to_act2(float a, float b)
+{
+    return (uint32_t)f32_to_act<DT>(a) | ((uint32_t)f32_to_act<DT>(b) << 16);
+}
+
+
+// ---------------------------------------------------------------------------
+// MFMA operand forms: one packed word -> eight activation-dtype values in word
+// order, each the nearest-even rounding of the exact (q - z) * s.
+// ---------------------------------------------------------------------------
+
+// binary16: exact pair (q - z) times the scale pair, one rounding (v_pk_mul_f16).
+__device__ __forceinline__ u32x4 w4_word_f16x8(uint32_t w, half2_t negbias, half2_t s2)
+{
+    const u32x4 b = nib_pairs_biased(w, MAGIC4_F16);
+    u32x4 o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        o[p] = bitcast<uint32_t>((bitcast<half2_t>(b[p]) + negbias) * s2);
+    return o;
+}
+
+// bfloat16: q as fp32 from a byte lane, minus z (exact), times s (exact: the
+// product fits in 24 bits, and a zero difference keeps the IEEE sign of
+// 0 * s), then one rounding to bfloat16.
+__device__ __forceinline__ u32x4 w4_word_bf16x8(uint32_t w, float s, float zf)
+{
+    const uint32_t lo = w & 0x0F0F0F0Fu;        // values 0, 2, 4, 6 in bytes 0..3
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu; // values 1, 3, 5, 7
+    const float q0 = (float)(lo & 0xFFu), q2 = (float)((lo >> 8) & 0xFFu);
+    const float q4 = (float)((lo >> 16) & 0xFFu), q6 = (float)(lo >> 24);
+    const float q1 = (float)(hi & 0xFFu), q3 = (float)((hi >> 8) & 0xFFu);
+    const float q5 = (float)((hi >> 16) & 0xFFu), q7 = (float)(hi >> 24);
+    u32x4 o;
+    o[0] = f32x2_to_act2<DT_BF16>((q0 - zf) * s, (q4 - zf) * s);
+    o[1] = f32x2_to_act2<DT_BF16>((q1 - zf) * s, (q5 - zf) * s);
+    o[2] = f32x2_to_act2<DT_BF16>((q2 - zf) * s, (q6 - zf) * s);
+    o[3] = f32x2_to_act2<DT_BF16>((q3 - zf) * s, (q7 - zf) * s);
+    return o;
+}
+
+// MXFP4: one word holds eight E2M1 elements in natural order (even element in
+// the low nibble of each byte).  v_cvt_scalef32_pk_bf16_fp4 converts the two
+// elements of one byte and multiplies them by the fp32 scale; the E8M0 byte
+// becomes that scale by being placed in the binary32 exponent field ("Add
+// BF16xFP4 MoE GEMM stage1 kernel", Technical Details).  Output pairs are in
+// natural order: (0,1) (2,3) (4,5) (6,7).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) { return bitcast<float>(b << 23); }
+
+__device__ __forceinline__ u32x4 fp4_word_bf16x8(uint32_t w, float scale)
+{
+    u32x4 o;
+    o[0] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+    o[1] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+    o[2] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+    o[3] = bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+    return o;
+}
+
+// Wave-wide helpers.
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+} // namespace wob

@@ -1,0 +1,44 @@
+// Host-side declarations shared by the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wob {
+
+struct W4Args {
+    const void *x;
+    const uint32_t *qweight;
+    const void *scales;
+    const uint32_t *qzeros; // nullptr: symmetric (z = 8)
+    void *y;
+    int dt; // DT_F16 / DT_BF16
+    int M, N, K, g;
+};
+
+// Skinny split-K GEMV (M <= 8).
+bool skinny_fits(int M, int N, int K, int g);
+hipError_t launch_w4a16_skinny(const W4Args &a, hipStream_t stream);
+
+// Cooperative-tile MFMA GEMM (any M).
+hipError_t launch_w4a16_tiled(const W4Args &a, hipStream_t stream);
+
+// Ragged grouped form of the tiled GEMM.
+hipError_t launch_w4a16_grouped(const W4Args &a, const int64_t *m_offsets, int num_groups,
+                                hipStream_t stream);
+
+// MoE stage 1, BF16 x MXFP4.
+size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+hipError_t launch_mxfp4_moe(const void *x, const int32_t *ids, const uint8_t *w_fp4,
+                            const uint8_t *w_scale, void *y, int T, int topk, int E, int N, int K,
+                            void *workspace, hipStream_t stream);
+
+// Dequantization probes.
+hipError_t launch_w4a16_dequant(const uint32_t *qweight, const void *scales, const uint32_t *qzeros,
+                                void *out, int dt, bool out_f32, int N, int K, int g,
+                                hipStream_t stream);
+hipError_t launch_mxfp4_dequant(const uint8_t *w_fp4, const uint8_t *w_scale, void *out, int N,
+                                int K, hipStream_t stream);
+
+} // namespace wob
