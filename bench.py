@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the weight-only 4-bit GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_gemv]
+
+Prints ONE JSON line.  A step is one call of the library on one batch of
+synthetic operands of the named workload (default: the decode GEMV
+1x43008x5376, g=32, fp16 -- the gate_up decode shape of the zero-point page,
+section Results).  Operands are rotated over enough device copies that the
+bytes touched between two uses of a copy exceed the 256 MB Infinity Cache, so
+the timing sees HBM, not cache.
+
+Timed region: K steps captured in one HIP graph and replayed once, bracketed
+by torch.cuda.synchronize(), with HIP events on the launch stream around the
+replay; `value` = algorithmic bytes (or FLOPs) per step / step time.  In the
+graph the kernels run back to back, so the step time is the kernel's average
+launch duration and the roofline entry uses it.  The CPU baseline is the
+oracle (single-threaded C) on the full decode call.
+
+Other workloads of the pages (tiny GEMV, small batch, prefill, MoE stage 1)
+are measured the same way and reported under "others".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as wl  # noqa: E402
+
+METRIC = ("µs/call + achieved HBM GB/s (M≤8) / TFLOP/s (M≥16), % of roofline")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA, published
+MALL_BYTES = 256 << 20         # Infinity Cache
+FETCH_FACTOR_DEFAULT = 2.0     # FETCH_SIZE reads half of a device copy's bytes on this part
+
+KERNEL_SOURCES = {
+    "w4a16": ["weight_only_bit_amd/csrc/skinny.hip", "weight_only_bit_amd/csrc/tiled.hip",
+              "weight_only_bit_amd/csrc/wob_device.hpp"],
+    "moe": ["weight_only_bit_amd/csrc/moe.hip", "weight_only_bit_amd/csrc/wob_device.hpp"],
+}
+
+
+def source_sha(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(key: str, kind: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if the
+    kernel sources are unchanged since the counters were taken; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(kind):
+        return None
+    factor = rec.get("fetch_factor", FETCH_FACTOR_DEFAULT)
+    return int(round((rec["fetch_kib"] * factor + rec["write_kib"]) * 1024))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _to_dev(d):
+    torch = _torch()
+    act = torch.float16 if d["dtype"] == wl.F16 else torch.bfloat16
+
+    def a(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(act).cuda()
+
+    return dict(x=a(d["x"]), qweight=torch.from_numpy(d["qweight"]).cuda(), scales=a(d["scales"]),
+                qzeros=None if d["qzeros"] is None else torch.from_numpy(d["qzeros"]).cuda())
+
+
+def _copies_for(bytes_per_call: int, max_copies: int = 256) -> int:
+    n = 1
+    while n * bytes_per_call < 2 * MALL_BYTES and n < max_copies:
+        n *= 2
+    return max(n, 2)
+
+
+def _time_steps(step, steps: int, warmup: int):
+    """Time exactly `steps` steps: captured into one HIP graph, replayed once
+    between two synchronizations, with HIP events recorded on the launch
+    stream around the replay.  Returns the average step time in ms (in the
+    graph the kernels run back to back, so this is the kernel's average
+    launch duration plus the command processor's gap between nodes, which
+    is zero for kernels longer than a few microseconds)."""
+    torch = _torch()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            step(i)
+    g.replay()  # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del g
+    return ms
+
+
+def bench_w4a16(wkey: str, steps: int, warmup: int):
+    import weight_only_bit_amd as wob
+    torch = _torch()
+    w = wl.BY_KEY[wkey]
+    d = w.make(seed=0)
+    M, N, K, g = d["M"], d["N"], d["K"], d["g"]
+    nbytes = wl.w4a16_bytes(M, N, K, g)
+    flops = 2 * M * N * K
+    copies = _copies_for(nbytes)
+    bufs = [_to_dev(d) for _ in range(copies)]
+    act = bufs[0]["x"].dtype
+    ys = [torch.empty((M, N), dtype=act, device="cuda") for _ in range(copies)]
+
+    def step(i):
+        b = bufs[i % copies]
+        wob.gemm(b["x"], b["qweight"], b["scales"], b["qzeros"], g, out=ys[i % copies])
+
+    graph_ms = kern_ms = _time_steps(step, steps, warmup)
+    skinny = M <= 8
+    res = dict(workload=w.desc, M=M, N=N, K=K, g=g, dtype=wl.DTYPE_NAMES[d["dtype"]],
+               copies=copies, bytes_per_call=nbytes, flops_per_call=flops,
+               us_per_call=round(graph_ms * 1e3, 3))
+    if skinny:
+        res["gbs"] = round(nbytes / (graph_ms * 1e-3) / 1e9, 1)
+        achieved = nbytes / (kern_ms * 1e-3) / 1e9
+        res["roofline"] = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                               unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                               traffic=committed_traffic(wkey, "w4a16"))
+    else:
+        res["tflops"] = round(flops / (graph_ms * 1e-3) / 1e12, 2)
+        achieved = flops / (kern_ms * 1e-3) / 1e12
+        res["roofline"] = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_PEAK_TFLOPS,
+                               unit="TFLOP/s", frac=round(achieved / MFMA_PEAK_TFLOPS, 4),
+                               traffic=committed_traffic(wkey, "w4a16"))
+    del bufs, ys
+    torch.cuda.empty_cache()
+    return res, d
+
+
+def bench_moe(wkey: str, steps: int, warmup: int):
+    import weight_only_bit_amd as wob
+    torch = _torch()
+    w = wl.BY_KEY[wkey]
+    d = w.make(seed=0)
+    T, E, topk, N, K = d["T"], d["E"], d["topk"], d["N"], d["K"]
+    nbytes = wl.moe_bytes(T, E, topk, N, K)
+    flops = 2 * T * topk * N * K
+    copies = _copies_for(nbytes, max_copies=4)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    bufs = []
+    for _ in range(copies):
+        bufs.append(dict(x=dev(d["x"].view(np.int16)).view(torch.bfloat16), ids=dev(d["ids"]),
+                         w=dev(d["w_fp4"]), s=dev(d["w_scale"])))
+    ys = [torch.empty((T, topk, N), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+    ws = torch.empty(max(wob.moe_workspace_size(T, topk, E), 16), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        b = bufs[i % copies]
+        wob.mxfp4_moe_gemm(b["x"], b["ids"], b["w"], b["s"], out=ys[i % copies], workspace=ws)
+
+    graph_ms = kern_ms = _time_steps(step, steps, warmup)
+    res = dict(workload=w.desc, T=T, E=E, topk=topk, N=N, K=K, dtype="bf16 x mxfp4",
+               copies=copies, bytes_per_call=nbytes, flops_per_call=flops,
+               us_per_call=round(graph_ms * 1e3, 3),
+               tflops=round(flops / (graph_ms * 1e-3) / 1e12, 2))
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    res["roofline"] = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_PEAK_TFLOPS,
+                           unit="TFLOP/s", frac=round(achieved / MFMA_PEAK_TFLOPS, 4),
+                           traffic=committed_traffic(wkey, "moe"))
+    del bufs, ys
+    torch.cuda.empty_cache()
+    return res, d
+
+
+def cpu_baseline_decode(d, budget_s: float = 10.0):
+    """The oracle as it stands, single-threaded, on the full decode call."""
+    import oracle
+    M, N, K, g = d["M"], d["N"], d["K"], d["g"]
+    nbytes = wl.w4a16_bytes(M, N, K, g)
+    times = []
+    t_start = time.perf_counter()
+    while not times or (time.perf_counter() - t_start < budget_s and len(times) < 5):
+        t0 = time.perf_counter()
+        oracle.w4a16_gemm(d["x"], d["dtype"], d["qweight"], d["scales"], d["qzeros"], M, N, K, g)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return dict(value=round(nbytes / t / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"full {M}x{N}x{K} g={g} call, median of {len(times)} runs "
+                       f"({t:.2f} s each) on one host thread")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_gemv", choices=[w.key for w in wl.WORKLOADS])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the weight-only GEMM path is single-GPU; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    torch = _torch()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import weight_only_bit_amd as wob
+    wob.device_check()
+
+    head = wl.BY_KEY[args.workload]
+    if head.kind == "w4a16":
+        res, d = bench_w4a16(head.key, args.steps, args.warmup)
+    else:
+        res, d = bench_moe(head.key, args.steps, args.warmup)
+    skinny = head.kind == "w4a16" and d["M"] <= 8
+    line = dict(
+        metric=METRIC,
+        value=res["gbs"] if skinny else res["tflops"],
+        unit="GB/s" if skinny else "TFLOP/s",
+        n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(res["us_per_call"] / 1e3, 6),
+        higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype=res["dtype"], data="synthetic",
+        config=dict(workload=res["workload"], **{k: res[k] for k in ("M", "N", "K", "g", "T", "E",
+                                                                     "topk") if k in res},
+                    copies=res["copies"], bytes_per_call=res["bytes_per_call"],
+                    flops_per_call=res["flops_per_call"]),
+        us_per_call=res["us_per_call"],
+        roofline=res["roofline"],
+    )
+    if not args.no_cpu_baseline and head.key == "decode_gemv":
+        line["cpu_baseline"] = cpu_baseline_decode(d)
+    else:
+        line["cpu_baseline"] = None
+    if not args.no_others:
+        others = {}
+        for w in wl.WORKLOADS:
+            if w.key == head.key:
+                continue
+            try:
+                r, _ = (bench_w4a16 if w.kind == "w4a16" else bench_moe)(w.key, args.steps, args.warmup)
+                others[w.key] = r
+            except Exception as e:  # report, do not hide: the entry says what failed
+                others[w.key] = dict(workload=w.desc, error=f"{type(e).__name__}: {e}")
+        line["others"] = others
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,97 @@
+"""GPU parity of the cooperative-tile MFMA W4A16 GEMM against the oracle.
+
+Covers every tile height (M up to 32, 64, 128, above), ragged M, N and K
+tails (N not a multiple of the 256-row tile, K not a multiple of the 128 span),
+g in {32, 64, 128}, fp16/bf16, symmetric codes and signed two-decade scales,
+plus the full prefill shape 2048x16384x5376 (g=128) on sampled outputs.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from tests.gpu_util import host_bits, is_nan_bits, require_gpu, torch_mod, w4a16_to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wob():
+    require_gpu()
+    import weight_only_bit_amd as w
+    w.device_check()
+    return w
+
+
+def _run(wob, d, path):
+    torch = torch_mod()
+    t = w4a16_to_device(d)
+    M, N = d["M"], d["N"]
+    out = torch.empty((M + 2, N), dtype=t["x"].dtype, device="cuda")
+    out.fill_(float("nan"))
+    wob.gemm(t["x"], t["qweight"], t["scales"], t["qzeros"], d["g"], out=out[1:M + 1], path=path)
+    torch.cuda.synchronize()
+    bits = host_bits(out)
+    assert np.all(is_nan_bits(bits[0], d["dtype"])) and np.all(is_nan_bits(bits[M + 1], d["dtype"]))
+    return bits[1:M + 1]
+
+
+def _check(oracle, d, ybits):
+    yref = oracle.w4a16_gemm(d["x"], d["dtype"], d["qweight"], d["scales"], d["qzeros"],
+                             d["M"], d["N"], d["K"], d["g"])
+    ok, err, bound = oracle.tolerance_ok(oracle.act_decode(ybits, d["dtype"]), yref)
+    assert ok, f"max err {err} > bound {bound}"
+
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("M", [1, 9, 16, 17, 33, 64, 100, 129, 256, 300])
+def test_tiled_m_sweep(wob, oracle, dtype, M):
+    d = wl.w4a16_inputs(M, 264, 544, 32, dtype, seed=M)
+    _check(oracle, d, _run(wob, d, wob.PATH_TILED))
+
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("g", [32, 64, 128])
+@pytest.mark.parametrize("N,K", [(8, 128), (24, 32), (256, 256), (520, 1088), (1024, 384)])
+def test_tiled_shapes(wob, oracle, dtype, g, N, K):
+    if K % g:
+        pytest.skip("K not a multiple of g")
+    d = wl.w4a16_inputs(40, N, K, g, dtype, seed=N + K + g)
+    _check(oracle, d, _run(wob, d, wob.PATH_TILED))
+
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+def test_tiled_symmetric_and_signed(wob, oracle, dtype):
+    d = wl.w4a16_inputs(70, 512, 512, 64, dtype, seed=5, symmetric=True)
+    _check(oracle, d, _run(wob, d, wob.PATH_TILED))
+    d = wl.w4a16_inputs(70, 512, 512, 128, dtype, seed=6, signed_scales=True)
+    _check(oracle, d, _run(wob, d, wob.PATH_TILED))
+
+
+def test_tiled_matches_skinny_on_small_m(wob):
+    """Both paths on the same M <= 8 input agree to the parity bound of each other."""
+    d = wl.w4a16_inputs(4, 512, 1024, 128, wl.F16, seed=3)
+    a = _run(wob, d, wob.PATH_TILED).view(np.float16).astype(np.float64)
+    b = _run(wob, d, wob.PATH_SKINNY).view(np.float16).astype(np.float64)
+    assert np.max(np.abs(a - b)) <= 1e-2 * np.max(np.abs(b)) + 1e-3
+
+
+def test_config_prefill_full_size(wob, oracle):
+    """2048x16384x5376 g=128 fp16: all outputs finite; 3000 sampled outputs
+    spread over every row/column tile against the oracle."""
+    d = wl.BY_KEY["prefill"].make()
+    ybits = _run(wob, d, wob.PATH_AUTO)
+    y = oracle.act_decode(ybits, d["dtype"])
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(0)
+    ns = np.sort(np.concatenate([[0, 255, 256, d["N"] - 1], rng.integers(0, d["N"], 2996)]))
+    ms = rng.integers(0, d["M"], ns.size)
+    ms[:4] = [0, 2047, 255, 256]
+    yref = oracle.w4a16_gemm_sampled(d["x"], d["dtype"], d["qweight"], d["scales"], d["qzeros"],
+                                     d["K"], d["g"], ms, ns)
+    ok, err, bound = oracle.tolerance_ok(y[ms, ns], yref)
+    assert ok, (err, bound)
+
+
+def test_tiled_deterministic(wob):
+    d = wl.w4a16_inputs(300, 520, 1088, 32, wl.BF16, seed=2)
+    assert np.array_equal(_run(wob, d, wob.PATH_TILED), _run(wob, d, wob.PATH_TILED))
