@@ -28,10 +28,12 @@
 //    staging registers), double buffered across spans.  Within a row the
 //    16-byte block b is stored at position b ^ (row % 16), which makes the
 //    operand reads (32 rows x one block each) bank-conflict free.
-//  * Software pipeline: while span s multiplies, the packed weights of span
-//    s+1 (loaded during span s-1) are dequantized a slice per activation
-//    block, between the MFMAs, and the loads of span s+2 are issued; the
-//    activation tile of span s+1 streams into the other LDS buffer.
+//  * Software pipeline: within a span the loop runs over the 8 MFMA steps;
+//    each step dequantizes the two weight words it needs (one per 32-row
+//    block) and issues its 2 x MB MFMAs, while the next step's activation
+//    operands are read from LDS and its two words are dequantized.  The raw
+//    packed weights are double buffered in registers and loaded a whole span
+//    ahead; the next span's activation tile streams into the other LDS buffer.
 //  * Tiles are mapped so that the workgroups running on one XCD share one
 //    activation M-tile in its L2.
 //  * Tails: weight rows >= N and activation rows >= M are clamped to valid
@@ -166,12 +168,6 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
     int tiles_per_xcd)
 {
     constexpr int TM = 32 * MB;
-    // The next span's 16 weight words are dequantized between the MFMAs of
-    // the first DQ activation blocks; only then are the next loads issued
-    // (register loads consumed while an LDS DMA is outstanding would force a
-    // full wait).
-    constexpr int DQ = MB >= 2 ? MB / 2 : 1;
-    constexpr int WPI = 16 / DQ;
     extern __shared__ __align__(16) uint8_t smem[]; // 2 x TM x 256 bytes
 
     // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD takes a
@@ -229,18 +225,18 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
             }
         }
     };
-    // Word i (0..15) of a span's operands: block i / 8, step i % 8.  Only a
-    // span that crosses K (uniform test) needs the per-lane zeroing of the
-    // 32-wide slices past K.
-    auto dequant_one = [&](const Raw &r, int span, int i, u32x4(&bop)[2][8]) __attribute__((always_inline)) {
-        const int nb = i >> 3, st = i & 7, hf = st >> 2;
+    // Operand of block nb, step st of a span: one weight word as 8 values.
+    // Only a span that crosses K (uniform test) needs the per-lane zeroing of
+    // the 32-wide slices past K.
+    auto dequant_op = [&](const Raw &r, int span, int nb, int st) __attribute__((always_inline)) {
+        const int hf = st >> 2;
         const uint32_t z = (r.z[nb][hf] >> zsh) & 0xFu;
         u32x4 v = dequant_word<DT>(r.w[nb][hf][st & 3], r.s[nb][hf], z);
         if (span * TL_SPAN + TL_SPAN > K) {
             if (span * TL_SPAN + 64 * h + 32 * hf >= K)
                 v = u32x4{0, 0, 0, 0};
         }
-        bop[nb][st] = v;
+        return v;
     };
 
     // ---- activation tile DMA: TM rows x 16 blocks per span, 1 KB per wave instruction ----
@@ -283,68 +279,77 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
             for (int e = 0; e < 16; ++e)
                 acc[nb][mb][e] = 0.f;
 
-    Raw raw;
-    u32x4 bopA[2][8], bopB[2][8]; // operands of the current / next span (ping-pong)
-    load_w(0, raw);
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-        dequant_one(raw, 0, i, bopA);
-    load_w(min(1, S - 1), raw);
-    wait_vmcnt<0>();
+    // Raw weights double buffered: rA / rB alternate between "this span"
+    // (complete) and "next span" (loads in flight).
+    Raw rA, rB;
+    load_w(0, rA);
+    load_w(min(1, S - 1), rB);
     issue_x(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     barrier_only();
 
-    // One span: MFMAs on LDS buffer span & 1 with operands `cur`; meanwhile
-    // the next span's tile streams into the other buffer, its weights (raw,
-    // loaded during the previous span) are dequantized into `nxt` between the
-    // MFMAs of the first DQ blocks, and then raw is refilled for span + 2.
-    auto run_span = [&](int span, const u32x4(&cur)[2][8], u32x4(&nxt)[2][8]) __attribute__((always_inline)) {
+    // One span: MFMAs on LDS buffer span & 1 with the weights in `cur`.  At
+    // entry `nxt`'s loads (span + 1) have landed; they are re-issued for
+    // span + 2 after this span's computation has read `cur`... the roles
+    // swap every span, so `cur` of this span is refilled for span + 2.
+    auto run_span = [&](int span, Raw &cur, Raw &nxt) __attribute__((always_inline)) {
+        (void)nxt;
         const int buf = span & 1;
-        wait_vmcnt<0>(); // raw complete (it was issued a span ago)
         issue_x(min(span + 1, S - 1), buf ^ 1);
         const uint8_t *xb = smem + (size_t)buf * TM * TL_ROWB;
-        // Activation operand of flat step q = 8 mb + s: 32 rows (nl) of block
-        // mb, 16-byte block 8h + s of the span; read two steps ahead.
-        auto read_x = [&](int q) __attribute__((always_inline)) {
-            const int R = 32 * (q >> 3) + nl;
-            const int p = (8 * h + (q & 7)) ^ (R & 15);
+        // Activation operand of block mb, step st: 32 rows (nl), 16-byte
+        // block 8h + st of the span.
+        auto read_x = [&](int mb, int st) __attribute__((always_inline)) {
+            const int R = 32 * mb + nl;
+            const int p = (8 * h + st) ^ (R & 15);
             return *reinterpret_cast<const u32x4 *>(xb + R * TL_ROWB + 16 * p);
         };
-        u32x4 xr[3];
-        xr[0] = read_x(0);
-        xr[1] = read_x(1);
+        u32x4 wc[2], wn[2], xc[MB], xn[MB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
+        for (int nb = 0; nb < 2; ++nb)
+            wc[nb] = dequant_op(cur, span, nb, 0);
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int q = 8 * mb + s;
-                if (q + 2 < 8 * MB)
-                    xr[(q + 2) % 3] = read_x(q + 2);
+        for (int mb = 0; mb < MB; ++mb)
+            xc[mb] = read_x(mb, 0);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            if (st < 7) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    xn[mb] = read_x(mb, st + 1);
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
-                    acc[nb][mb] = mfma32x32x16<DT>(cur[nb][s], xr[q % 3], acc[nb][mb]);
+                    wn[nb] = dequant_op(cur, span, nb, st + 1);
             }
-            if (mb < DQ) {
 #pragma unroll
-                for (int i = 0; i < WPI; ++i)
-                    dequant_one(raw, span + 1, mb * WPI + i, nxt);
-            }
-            if (mb == DQ - 1)
-                load_w(min(span + 2, S - 1), raw);
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[nb][mb] = mfma32x32x16<DT>(wc[nb], xc[mb], acc[nb][mb]);
             __builtin_amdgcn_sched_barrier(0);
+            if (st < 7) {
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    wc[nb] = wn[nb];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    xc[mb] = xn[mb];
+            }
         }
-        __builtin_amdgcn_s_waitcnt(0); // this span's DMA and the raw refill
+        // `cur` is consumed: refill it for span + 2 (clamped, so the wait
+        // counts stay exact), then the barrier that publishes the next tile.
+        load_w(min(span + 2, S - 1), cur);
+        wait_vmcnt<HAS_Z ? 12 : 8>(); // everything but the refill: next tile + nxt
         barrier_only();
     };
 
     int span = 0;
     for (; span + 1 < S; span += 2) {
-        run_span(span, bopA, bopB);
-        run_span(span + 1, bopB, bopA);
+        run_span(span, rA, rB);
+        run_span(span + 1, rB, rA);
     }
     if (span < S)
-        run_span(span, bopA, bopB);
+        run_span(span, rA, rB);
 
     // ---- epilogue: lane holds D[n = 8 g + 4 h + j][m = nl], register 4 g + j ----
 #pragma unroll
