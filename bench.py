@@ -228,6 +228,9 @@ def main():
     ap.add_argument("--workload", default="decode_gemv", choices=[w.key for w in wl.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before timing, run three device-to-device copies of this many MiB "
+                         "(untimed): the known-size reference for the profiler's byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -242,6 +245,14 @@ def main():
         sys.exit(1)
     import weight_only_bit_amd as wob
     wob.device_check()
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     head = wl.BY_KEY[args.workload]
     if head.kind == "w4a16":

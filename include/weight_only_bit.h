@@ -92,7 +92,8 @@ int wob_device_check(void);
  *  zeros_dtype: WOB_U4X8_I32 (ignored when qzeros == NULL); any other tag
  *    -> WOB_DTYPE (activation-dtype zero-points are refused, not reinterpreted).
  *  group_size in {32, 64, 128} (else WOB_UNSUPPORTED); K % group_size == 0,
- *    K % 32 == 0, N % 8 == 0, M >= 0, N >= 0, K >= 32 (else WOB_INVALID_ARG).
+ *    K % 32 == 0, N % 8 == 0, M >= 0, N >= 0, K >= 32, N*K/2 below 2^32
+ *    (else WOB_INVALID_ARG).
  *    M == 0 or N == 0 is a no-op returning WOB_OK.
  *  Accumulation is fp32; y is rounded to nearest even in x's dtype.
  */
@@ -133,7 +134,9 @@ size_t mxfp4_moe_gemm_workspace_size(int64_t T, int64_t topk, int64_t E);
  *
  *  x [T][K] bf16; topk_ids [T][topk] int32 on the device; y [T][topk][N] bf16.
  *  Rows whose id lies outside [0, E) are written as zeros.
- *  K % 32 == 0, K >= 32, N % 16 == 0, T >= 0, 1 <= topk, 1 <= E (else WOB_INVALID_ARG).
+ *  K % 64 == 0 (the page's 64-wide K tile), K >= 64, N % 16 == 0, T >= 0,
+ *  1 <= topk <= 64, 1 <= E <= 4096, T*K*2 and N*K/2 below 2^32 (else
+ *  WOB_INVALID_ARG).
  *  workspace: device memory of at least mxfp4_moe_gemm_workspace_size(T, topk, E)
  *  bytes, 16-byte aligned (else WOB_INVALID_ARG); its contents on entry do not
  *  matter.  Calls that share one workspace must be ordered on one stream.

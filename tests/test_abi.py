@@ -102,7 +102,9 @@ def test_moe_checks(L):
     assert L.lib().mxfp4_moe_gemm_workspace_size(-1, 4, 32) == 0
     call = lambda K=64, N=32, ws=need, T=4: L.lib().mxfp4_moe_gemm(p, p, p, p, p, T, 4, 32, N, K, p, ws, None)
     assert call(K=48) == L.INVALID_ARG
+    assert call(K=96) == L.INVALID_ARG  # the K tile is 64 wide
     assert call(N=24) == L.INVALID_ARG
+    assert call(T=1 << 21, K=1 << 11) == L.INVALID_ARG  # x past 32-bit byte offsets
     assert call(ws=0) == L.INVALID_ARG
     assert call(T=0) == L.OK
 

@@ -1,0 +1,136 @@
+"""GPU parity of MoE stage 1 (BF16 x MXFP4, routed) against the oracle, through
+the C ABI.
+
+Bar: |y - y_ref| <= 1e-3 + 1e-2 * max|y_ref| per element, no NaN/Inf, and every
+(token, slot) row written exactly where it belongs.  The matrix follows the
+MXFP4 MoE page (section Test: tile heights 16, 32 and 64 rows per expert; the
+store-guard fix for a tile that overhangs the weight rows) widened to skewed
+and empty experts, top-1 routing, out-of-range ids, ragged N and K, and the
+full 1024-token, 32-expert, top-4, K=2880, N=5760 shape on sampled outputs.
+"""
+import numpy as np
+import pytest
+
+import workloads as wl
+from tests.gpu_util import dev, host_bits, is_nan_bits, require_gpu, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wob():
+    require_gpu()
+    import weight_only_bit_amd as w
+    w.device_check()
+    return w
+
+
+def _run(wob, d, ids=None):
+    """Run with NaN-filled guard rows around y; return y's bf16 bits [T, topk, N]."""
+    torch = torch_mod()
+    T, topk, N = d["T"], d["topk"], d["N"]
+    ids = d["ids"] if ids is None else ids
+    out = torch.empty((T * topk + 2, N), dtype=torch.bfloat16, device="cuda")
+    out.fill_(float("nan"))
+    y = out[1:T * topk + 1].view(T, topk, N)
+    x = dev(d["x"].view(np.int16)).view(torch.bfloat16)
+    wob.mxfp4_moe_gemm(x, dev(ids), dev(d["w_fp4"]), dev(d["w_scale"]), out=y)
+    torch.cuda.synchronize()
+    bits = host_bits(out)
+    assert np.all(is_nan_bits(bits[0], wl.BF16)), "write before y"
+    assert np.all(is_nan_bits(bits[-1], wl.BF16)), "write after y"
+    return bits[1:-1].reshape(T, topk, N)
+
+
+def _check(oracle, d, ybits, ids=None):
+    ids = d["ids"] if ids is None else ids
+    yref = oracle.mxfp4_moe_gemm(d["x"], ids, d["w_fp4"], d["w_scale"], d["T"], d["topk"],
+                                 d["E"], d["N"], d["K"])
+    y = oracle.bf16_decode(ybits)
+    ok, err, bound = oracle.tolerance_ok(y, yref)
+    assert ok, f"max err {err} > bound {bound}"
+    return y, yref
+
+
+@pytest.mark.parametrize("T,E,topk,N,K", [(64, 8, 2, 512, 256), (37, 4, 3, 400, 192),
+                                          (200, 16, 4, 256, 2880), (5, 32, 4, 48, 64)])
+def test_moe_random_routing(wob, oracle, T, E, topk, N, K):
+    d = wl.moe_inputs(T, E, topk, N, K, seed=T + N)
+    _check(oracle, d, _run(wob, d))
+
+
+@pytest.mark.parametrize("rows_per_expert", [16, 32, 64, 100, 256, 257])
+def test_moe_tile_heights(wob, oracle, rows_per_expert):
+    """Every expert gets exactly `rows_per_expert` rows (the page's tile heights
+    16/32/64, a ragged 100, one full 256-row tile and one row past it)."""
+    E, topk = 4, 1
+    T = E * rows_per_expert
+    d = wl.moe_inputs(T, E, topk, 528, 320, seed=rows_per_expert)
+    ids = (np.arange(T) % E).astype(np.int32).reshape(T, 1)
+    _check(oracle, d, _run(wob, d, ids), ids)
+
+
+def test_moe_skewed_and_empty_experts(wob, oracle):
+    """All tokens on one expert (two 256-row tiles plus a tail) while the other
+    experts stay empty."""
+    d = wl.moe_inputs(600, 8, 1, 256, 128, seed=11)
+    ids = np.full((600, 1), 5, np.int32)
+    _check(oracle, d, _run(wob, d, ids), ids)
+
+
+def test_moe_top1_single_expert_is_dense(wob, oracle):
+    d = wl.moe_inputs(96, 1, 1, 272, 256, seed=3)
+    ids = np.zeros((96, 1), np.int32)
+    y, _ = _check(oracle, d, _run(wob, d, ids), ids)
+    dense = d["x"].astype(np.uint32) << 16
+    xf = dense.view(np.float32).astype(np.float64)
+    w = oracle.mxfp4_dequant(d["w_fp4"][0], d["w_scale"][0], 272, 256).astype(np.float64)
+    ref = xf @ w.T
+    assert np.max(np.abs(y[:, 0, :] - ref)) <= 1e-3 + 1e-2 * np.max(np.abs(ref))
+
+
+def test_moe_out_of_range_ids_write_zero_rows(wob, oracle):
+    d = wl.moe_inputs(40, 6, 2, 304, 128, seed=7)
+    ids = d["ids"].copy()
+    ids[0, 0] = -1
+    ids[3, 1] = 6
+    ids[17, 0] = 1000
+    ids[39, 1] = -2147483648
+    ybits = _run(wob, d, ids)
+    y, _ = _check(oracle, d, ybits, ids)
+    for t, s in [(0, 0), (3, 1), (17, 0), (39, 1)]:
+        assert np.all(ybits[t, s] == 0), (t, s)
+
+
+def test_moe_zero_tokens_is_noop(wob):
+    torch = torch_mod()
+    d = wl.moe_inputs(1, 2, 1, 64, 64, seed=0)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((0, 1), dtype=torch.int32, device="cuda")
+    y = wob.mxfp4_moe_gemm(x, ids, dev(d["w_fp4"]), dev(d["w_scale"]))
+    assert y.shape == (0, 1, 64)
+
+
+def test_moe_deterministic(wob):
+    d = wl.moe_inputs(300, 8, 4, 528, 384, seed=5)
+    assert np.array_equal(_run(wob, d), _run(wob, d))
+
+
+def test_config_moe_stage1_full_size(wob, oracle):
+    """1024 tokens, 32 experts, top-4, K=2880, N=5760: every output finite, 3000
+    sampled (token, slot, n) outputs against the oracle."""
+    d = wl.BY_KEY["moe_stage1"].make()
+    ybits = _run(wob, d)
+    y = oracle.bf16_decode(ybits)
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(0)
+    T, topk, N = d["T"], d["topk"], d["N"]
+    ts = rng.integers(0, T, 3000)
+    ss = rng.integers(0, topk, 3000)
+    ns = rng.integers(0, N, 3000)
+    ts[:3], ss[:3], ns[:3] = [0, T - 1, 5], [0, topk - 1, 1], [0, N - 1, 5759 - 128]
+    yref = oracle.mxfp4_moe_gemm_sampled(d["x"], d["ids"], d["w_fp4"], d["w_scale"], topk, d["E"],
+                                         N, d["K"], ts, ss, ns)
+    # the bound takes the sampled outputs' max|y_ref|: no looser than the global one
+    ok, err, bound = oracle.tolerance_ok(y[ts, ss, ns], yref)
+    assert ok, (err, bound)

@@ -6,6 +6,7 @@
 #include "wob_internal.hpp"
 
 #include <limits.h>
+#include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -86,7 +87,8 @@ int check_w4(const void *x, int x_dtype, const int32_t *qweight, const void *sca
                     (long long)K, (long long)g);
     if (N % 8 != 0)
         return fail(WOB_INVALID_ARG, "N=%lld is not a multiple of 8", (long long)N);
-    if (M > INT_MAX / 2 || N > INT_MAX / 2 || K > INT_MAX / 2 || (N / 8) * K > (int64_t)INT_MAX * 8)
+    // 32-bit in-kernel offsets into one matrix of packed codes (N*K/2 bytes)
+    if (M > INT_MAX / 2 || N > INT_MAX / 2 || K > INT_MAX / 2 || N * (K / 2) > (int64_t)UINT32_MAX)
         return fail(WOB_INVALID_ARG, "shape too large");
     if (M == 0 || N == 0)
         return WOB_OK;
@@ -210,10 +212,13 @@ int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
     if (T < 0 || topk < 1 || E < 1 || N < 0 || K < 32)
         return fail(WOB_INVALID_ARG, "bad shape T=%lld topk=%lld E=%lld N=%lld K=%lld",
                     (long long)T, (long long)topk, (long long)E, (long long)N, (long long)K);
-    if (K % 32 != 0 || N % 16 != 0)
-        return fail(WOB_INVALID_ARG, "need K %% 32 == 0 and N %% 16 == 0 (K=%lld N=%lld)",
+    if (K % 64 != 0 || N % 16 != 0)
+        return fail(WOB_INVALID_ARG, "need K %% 64 == 0 and N %% 16 == 0 (K=%lld N=%lld)",
                     (long long)K, (long long)N);
+    // 32-bit in-kernel offsets: x rows (T*K*2 bytes), one expert's codes
+    // (N*K/2 bytes) and the routed pair count T*topk.
     if (T > INT_MAX / 64 || topk > 64 || E > 4096 || N > INT_MAX / 2 || K > INT_MAX / 2 ||
+        T * K * 2 > (int64_t)UINT32_MAX || N * (K / 2) > (int64_t)UINT32_MAX ||
         E * N * (K / 2) > ((int64_t)1 << 40))
         return fail(WOB_INVALID_ARG, "shape too large");
     if (T == 0 || N == 0)

@@ -4,7 +4,8 @@
 //
 //  * W4A16, fp32 form: the skinny kernel's biased pair (B + q) minus (B + z),
 //    exact in fp32, times the fp32 scale.
-//  * W4A16, activation form: the tiled kernel's MFMA B-operand values.
+//  * W4A16, activation form: the tiled kernels' MFMA weight-operand values
+//    (w4_word_act8, the helper those kernels call).
 //  * MXFP4: the MoE kernel's B-operand values.
 // One thread per packed word; outputs are written in natural k order.
 #include "wob_device.hpp"
@@ -53,19 +54,12 @@ __global__ __launch_bounds__(256) void w4a16_dequant_kernel(
         for (int i = 0; i < 8; ++i)
             o[i] = vals[i];
     } else {
-        u32x4 v;
-        if constexpr (DT == DT_F16) {
-            const _Float16 sh = bitcast<_Float16>(sbits);
-            v = w4_word_f16x8(w, f16_neg_bias(z), half2_t{sh, sh});
-        } else {
-            const float s = act_to_f32<DT_BF16>(sbits);
-            v = w4_word_bf16x8(w, s, (float)z);
-        }
+        const u32x4 v = w4_word_act8<DT>(w, sbits, z); // natural k order
         uint16_t o16[8];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            o16[word_order_value(2 * p)] = (uint16_t)(v[p] & 0xFFFFu);
-            o16[word_order_value(2 * p + 1)] = (uint16_t)(v[p] >> 16);
+            o16[2 * p] = (uint16_t)(v[p] & 0xFFFFu);
+            o16[2 * p + 1] = (uint16_t)(v[p] >> 16);
         }
         uint16_t *o = static_cast<uint16_t *>(out) + (size_t)idx * 8;
 #pragma unroll

@@ -82,11 +82,6 @@ __device__ __forceinline__ u32x4 nib_pairs_biased(uint32_t w, uint32_t magic4)
 // Zero-point of row r (0..7) in a packed zero-point word.
 __device__ __forceinline__ uint32_t nib(uint32_t w, int r) { return (w >> (4 * r)) & 0xFu; }
 
-// binary16 pair (-(1024+z), -(1024+z)): adding it to a biased pair gives q - z.
-__device__ __forceinline__ half2_t f16_neg_bias(uint32_t z)
-{
-    return bitcast<half2_t>((0xE400u | z) * 0x00010001u);
-}
 
 // ---------------------------------------------------------------------------
 // Activation conversions
@@ -126,38 +121,64 @@ __device__ __forceinline__ uint32_t f32x2_to_act2(float a, float b)
 
 
 // ---------------------------------------------------------------------------
-// MFMA operand forms: one packed word -> eight activation-dtype values in word
-// order, each the nearest-even rounding of the exact (q - z) * s.
+// MFMA operand forms: one packed word -> eight activation-dtype values in
+// natural k order (value 2p and 2p+1 in 32-bit lane p), each the nearest-even
+// rounding of the exact (q - z) * s.
 // ---------------------------------------------------------------------------
 
-// binary16: exact pair (q - z) times the scale pair, one rounding (v_pk_mul_f16).
-__device__ __forceinline__ u32x4 w4_word_f16x8(uint32_t w, half2_t negbias, half2_t s2)
+// binary16: byte p of the word holds values 2p (low nibble) and 2p+1 (high
+// nibble); one permute places it twice next to the binary16 exponent byte
+// 0x64 and one mask keeps the low nibble in the first half and the high
+// nibble (times 16) in the second: the exact halves (1024 + q_even,
+// 1024 + 16 q_odd).  A packed fma with (1, 1/16) and -(1024 + z, 64 + z)
+// gives the exact (q - z) pair, and a packed multiply by the scale rounds once.
+__device__ __forceinline__ u32x4 w4_word_f16x8(uint32_t w, half2_t negb, half2_t s2)
 {
-    const u32x4 b = nib_pairs_biased(w, MAGIC4_F16);
+    const half2_t mul = half2_t{(_Float16)1.0f, (_Float16)0.0625f};
     u32x4 o;
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-        o[p] = bitcast<uint32_t>((bitcast<half2_t>(b[p]) + negbias) * s2);
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t sel = 0x04000400u | (uint32_t)p | ((uint32_t)p << 16);
+        const uint32_t t = __builtin_amdgcn_perm(MAGIC4_F16, w, sel) & 0xFFF0FF0Fu;
+        const half2_t d = __builtin_elementwise_fma(bitcast<half2_t>(t), mul, negb);
+        o[p] = bitcast<uint32_t>(d * s2);
+    }
     return o;
 }
 
-// bfloat16: q as fp32 from a byte lane, minus z (exact), times s (exact: the
+// The binary16 pair -(1024 + z, 64 + z) used by w4_word_f16x8.
+__device__ __forceinline__ half2_t f16_neg_bias_pair(uint32_t z)
+{
+    return bitcast<half2_t>((0xE400u | z) | ((0xD400u | (z << 4)) << 16));
+}
+
+// bfloat16: values from byte lanes as fp32, (q - z) * s exact in fp32 (the
 // product fits in 24 bits, and a zero difference keeps the IEEE sign of
-// 0 * s), then one rounding to bfloat16.
+// 0 * s), one rounding to bfloat16 per value.
 __device__ __forceinline__ u32x4 w4_word_bf16x8(uint32_t w, float s, float zf)
 {
-    const uint32_t lo = w & 0x0F0F0F0Fu;        // values 0, 2, 4, 6 in bytes 0..3
+    const uint32_t lo = w & 0x0F0F0F0Fu;        // values 0, 2, 4, 6
     const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu; // values 1, 3, 5, 7
-    const float q0 = (float)(lo & 0xFFu), q2 = (float)((lo >> 8) & 0xFFu);
-    const float q4 = (float)((lo >> 16) & 0xFFu), q6 = (float)(lo >> 24);
-    const float q1 = (float)(hi & 0xFFu), q3 = (float)((hi >> 8) & 0xFFu);
-    const float q5 = (float)((hi >> 16) & 0xFFu), q7 = (float)(hi >> 24);
     u32x4 o;
-    o[0] = f32x2_to_act2<DT_BF16>((q0 - zf) * s, (q4 - zf) * s);
-    o[1] = f32x2_to_act2<DT_BF16>((q1 - zf) * s, (q5 - zf) * s);
-    o[2] = f32x2_to_act2<DT_BF16>((q2 - zf) * s, (q6 - zf) * s);
-    o[3] = f32x2_to_act2<DT_BF16>((q3 - zf) * s, (q7 - zf) * s);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float qe = (float)((lo >> (8 * p)) & 0xFFu);
+        const float qo = (float)((hi >> (8 * p)) & 0xFFu);
+        o[p] = f32x2_to_act2<DT_BF16>((qe - zf) * s, (qo - zf) * s);
+    }
     return o;
+}
+
+// One weight word of the MFMA operand form from the scale bits and zero-point.
+template <int DT>
+__device__ __forceinline__ u32x4 w4_word_act8(uint32_t w, uint32_t sbits, uint32_t z)
+{
+    if constexpr (DT == DT_F16) {
+        const _Float16 sh = bitcast<_Float16>((uint16_t)sbits);
+        return w4_word_f16x8(w, f16_neg_bias_pair(z), half2_t{sh, sh});
+    } else {
+        return w4_word_bf16x8(w, act_to_f32<DT_BF16>((uint16_t)sbits), (float)z);
+    }
 }
 
 // MXFP4: one word holds eight E2M1 elements in natural order (even element in

@@ -1,0 +1,430 @@
+// Cooperative-tile MFMA pipeline for gfx950, shared by the dense W4A16 GEMM,
+// its ragged grouped form and the MXFP4 MoE stage-1 GEMM.
+//
+// Mechanism (cooperative shared tile: "ROCm KQuantGemmKWmmaQ4K/Q6K: redesign
+// around a cooperative shared tile, matching llama.cpp's mul_mat_q
+// mechanism", sections Confirmed mechanism and The work): one workgroup owns
+// a 256 x TM output tile (weight rows x activation rows).  The packed weights
+// of its 256 rows are loaded and dequantized exactly once, split across the
+// waves so no wave repeats another's work; one copy of the activation tile in
+// LDS serves every wave; each wave multiplies its own weight rows against the
+// whole activation range.  Dequantization and the matrix multiply are
+// separate steps ("ROCm IQ4_XS keep-quant GEMM is 8.8x behind llama.cpp's
+// WMMA path", section Cause), here registers -> MFMA operands.
+//
+// gfx950 realisation:
+//  * Matrix core: v_mfma_f32_32x32x16_{f16,bf16} (32 cycles each, measured
+//    with the MFMA busy counter), so every tile is built from 32 x 32 blocks.
+//  * 4 waves; wave w owns weight rows n0 + 64 w .. +63 (two 32-row blocks nb)
+//    and all TM = 32 * MB activation rows of the tile: 2 x MB accumulator
+//    blocks of 16 fp32 registers.
+//  * K advances in spans of 128 (8 MFMA steps of 16).  Lane (nl, h) =
+//    (lane % 32, lane / 32) loads 32 bytes of weight row nl of each block:
+//    words 8h .. 8h+7 of the span, i.e. k = 64h .. 64h+63 of the span, as two
+//    16-byte halves hf (32 k each).  MFMA step s uses word s of that load:
+//    operand slot (h, e) holds k = 64h + 8s + e.  The activation operand uses
+//    the same slots, so the pairing of k values is the same on both sides.
+//  * The activation tile (TM rows x 128 k, 256 bytes per row) is copied from
+//    global memory straight into LDS with global_load_lds_dwordx4 (no staging
+//    registers), double buffered across spans.  Within a row the 16-byte block
+//    b is stored at position b ^ (row % 16), which makes the operand reads
+//    (32 rows x one block each) bank-conflict free.  Rows come from a per-lane
+//    byte offset supplied by the caller, so the same copy serves contiguous
+//    rows and gathered (routed) rows.
+//  * Software pipeline: within a span the loop runs over the 8 MFMA steps;
+//    each step dequantizes the two weight words it needs (one per 32-row
+//    block) and issues its 2 x MB MFMAs, while the next step's activation
+//    operands are read from LDS and its two words are dequantized.  The raw
+//    packed weights are double buffered in registers and loaded a whole span
+//    ahead; the next span's activation tile streams into the other LDS buffer.
+//  * Tails: weight rows past the matrix are clamped to valid addresses and
+//    never stored; activation rows past the tile's row count are clamped to a
+//    valid row and never stored; a 32-wide K slice past K gets zero weights.
+//
+// Weight formats plug in as a policy with:
+//    struct Raw;                          raw loads of one span for one lane
+//    static constexpr int NLOADS;         vector-memory operations per load()
+//    void load(int span, Raw &r) const;   issue this lane's loads of a span
+//    u32x4 dequant(const Raw &, int nb, int st) const;  8 operand values
+#pragma once
+
+#include "wob_device.hpp"
+
+namespace wob {
+
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+constexpr int TL_WAVES = 4;
+constexpr int TL_THREADS = 64 * TL_WAVES;
+constexpr int TL_TN = 64 * TL_WAVES; // weight rows per workgroup
+constexpr int TL_SPAN = 128;         // K per span
+constexpr int TL_ROWB = 256;         // LDS bytes per activation row of a span
+constexpr int TL_MB_MAX = 8;         // largest tile: 256 activation rows
+
+// LDS bytes of a tile with up to mb_max 32-row blocks (two span buffers).
+__host__ __device__ constexpr int tile_lds_bytes(int mb_max) { return 2 * 32 * mb_max * TL_ROWB; }
+
+// s_waitcnt that waits until at most `n` vector-memory operations are
+// outstanding (expcnt and lgkmcnt left alone; gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the full memory wait __syncthreads() implies;
+// callers wait for exactly the operations the barrier must cover first.
+__device__ __forceinline__ void barrier_only()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane L's bytes land
+// at LDS byte address `lds_addr` + 16 L (global_load_lds_dwordx4, address =
+// `sbase` + `voff`).  Issued through inline asm on purpose: the compiler's
+// wait-count bookkeeping, once it sees an LDS DMA in flight, stops trusting
+// in-order completion and waits for everything before any later load result
+// or LDS read is used, which serializes the software pipeline.  The hardware
+// tracks the DMA with vmcnt only; every caller waits for it explicitly
+// (s_waitcnt vmcnt) before the destination is read.  M0 is saved and restored.
+__device__ __forceinline__ void lds_dma16(const void *sbase_any, uint32_t voff, uint32_t lds_addr)
+{
+    // the base must live in scalar registers: make its (uniform) value explicit
+    const uint64_t b = reinterpret_cast<uint64_t>(sbase_any);
+    // readfirstlane returns a signed int: zero-extend each half explicitly
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
+    const void *sbase = reinterpret_cast<const void *>(bu);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %1\n\t"
+                 "global_load_lds_dwordx4 %2, %3\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(sbase)
+                 : "memory");
+}
+
+template <int DT>
+__device__ __forceinline__ float16_t mfma32x32x16(const u32x4 &a, const u32x4 &b, const float16_t &c)
+{
+    if constexpr (DT == DT_F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<half8_t>(a), bitcast<half8_t>(b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf168_t>(a), bitcast<bf168_t>(b), c, 0, 0, 0);
+}
+
+// Lane coordinates inside the tile.
+struct TileLane {
+    int wave, lane, nl, h;
+    int rl;   // activation row (mod 16) this lane copies in every DMA instruction
+    int xblk; // 16-byte block of that row this lane copies
+    __device__ TileLane()
+    {
+        wave = threadIdx.x >> 6;
+        lane = threadIdx.x & 63;
+        nl = lane & 31;
+        h = lane >> 5;
+        rl = 4 * wave + (lane >> 4);
+        xblk = (lane & 15) ^ rl;
+    }
+};
+
+// First activation row of DMA instruction i for this lane is row 16 i + rl.
+// `XRows` supplies the byte offset (from `xbase`) of activation row r of the
+// tile, already clamped to a valid row:  uint32_t XRows::off(int i) const
+// returns the offset of row 16 i + rl for this lane.
+//
+// The tile body: runs the whole K loop for one 256 x (32 MB) tile and leaves
+// the accumulators in `acc`.  `Fmt` holds this lane's weight addressing.
+template <int DT, int MB, class Fmt, class XRows>
+__device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
+                                              const uint8_t *xbase, int K, uint8_t *smem,
+                                              const TileLane &tl, float16_t (&acc)[2][MB])
+{
+    constexpr int TM = 32 * MB;
+    const int S = (K + TL_SPAN - 1) / TL_SPAN;
+    const uint32_t lds0 = (uint32_t)(size_t)(lds_ptr_t *)smem;
+
+    // Activation tile DMA: TM rows x 16 blocks per span, 1 KB per wave
+    // instruction.  Instruction i of wave w fills LDS rows 16 i + 4 w .. +3;
+    // lane L takes row 16 i + rl and position L % 16, which holds global block
+    // (L % 16) ^ rl of that row.  Blocks past K are clamped inside the row
+    // (they meet zero weights).
+    auto issue_x = [&](int span, int buf) __attribute__((always_inline)) {
+        const uint32_t ldsb = lds0 + (uint32_t)(buf * TM * TL_ROWB);
+        const uint32_t kb = 2u * (uint32_t)min(span * TL_SPAN + 8 * tl.xblk, K - 8);
+#pragma unroll
+        for (int i = 0; i < TM / 16; ++i)
+            lds_dma16(xbase, xr.off(i) + kb,
+                      __builtin_amdgcn_readfirstlane(ldsb + (uint32_t)((16 * i + 4 * tl.wave) * TL_ROWB)));
+    };
+
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[nb][mb][e] = 0.f;
+
+    // Raw weights double buffered: rA / rB alternate between "this span"
+    // (complete) and "next span" (loads in flight).
+    typename Fmt::Raw rA, rB;
+    fmt.load(0, rA);
+    fmt.load(min(1, S - 1), rB);
+    issue_x(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    barrier_only();
+
+    // One span: MFMAs on LDS buffer span & 1 with the weights in `cur`.  At
+    // entry the next span's raw weights (the other buffer) have landed or are
+    // in flight; this span's `cur` is refilled for span + 2 once consumed.
+    auto run_span = [&](int span, typename Fmt::Raw &cur) __attribute__((always_inline)) {
+        const int buf = span & 1;
+        issue_x(min(span + 1, S - 1), buf ^ 1);
+        const uint8_t *xb = smem + (size_t)buf * TM * TL_ROWB;
+        // Activation operand of block mb, step st: 32 rows (nl), 16-byte
+        // block 8h + st of the span.
+        auto read_x = [&](int mb, int st) __attribute__((always_inline)) {
+            const int R = 32 * mb + tl.nl;
+            const int p = (8 * tl.h + st) ^ (R & 15);
+            return *reinterpret_cast<const u32x4 *>(xb + R * TL_ROWB + 16 * p);
+        };
+        const bool ktail = span * TL_SPAN + TL_SPAN > K;
+        auto dq = [&](int nb, int st) __attribute__((always_inline)) {
+            u32x4 v = fmt.dequant(cur, nb, st);
+            // only a span that crosses K (uniform test) zeroes the slices past K
+            if (ktail && span * TL_SPAN + 64 * tl.h + 32 * (st >> 2) >= K)
+                v = u32x4{0, 0, 0, 0};
+            return v;
+        };
+        u32x4 wc[2], wn[2], xc[MB], xn[MB];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+            wc[nb] = dq(nb, 0);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            xc[mb] = read_x(mb, 0);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            if (st < 7) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    xn[mb] = read_x(mb, st + 1);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    wn[nb] = dq(nb, st + 1);
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[nb][mb] = mfma32x32x16<DT>(wc[nb], xc[mb], acc[nb][mb]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (st < 7) {
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    wc[nb] = wn[nb];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    xc[mb] = xn[mb];
+            }
+        }
+        // `cur` is consumed: refill it for span + 2 (clamped, so the wait
+        // counts stay exact), then the barrier that publishes the next tile:
+        // wait for everything but that refill (next activation tile + the
+        // next span's weights).
+        fmt.load(min(span + 2, S - 1), cur);
+        wait_vmcnt<Fmt::NLOADS>();
+        barrier_only();
+    };
+
+    int span = 0;
+    for (; span + 1 < S; span += 2) {
+        run_span(span, rA);
+        run_span(span + 1, rB);
+    }
+    if (span < S)
+        run_span(span, rA);
+    // Only the last (clamped, duplicate) weight refill can still be in flight
+    // here; it targets registers, which the compiler's own wait counts cover.
+    // Every activation copy into LDS has been waited for.
+}
+
+// Store one tile's accumulators: lane holds D[n = 8 g4 + 4 h + j][m = nl] of
+// block (nb, mb) in register 4 g4 + j.  `yrow(r)` returns the output row
+// pointer of tile row r, called only for r < rows.
+template <int DT, int MB, class YRows>
+__device__ __forceinline__ void tile_store(const float16_t (&acc)[2][MB], const YRows &yr, int rows,
+                                          int n0, int N, const TileLane &tl)
+{
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int r = 32 * mb + tl.nl;
+        if (r >= rows)
+            continue;
+        uint16_t *yp = yr.row(r);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int n = n0 + 64 * tl.wave + 32 * nb + 8 * g4 + 4 * tl.h;
+                if (n >= N)
+                    continue;
+                const float16_t &v = acc[nb][mb];
+                uint2 o;
+                o.x = f32x2_to_act2<DT>(v[4 * g4 + 0], v[4 * g4 + 1]);
+                o.y = f32x2_to_act2<DT>(v[4 * g4 + 2], v[4 * g4 + 3]);
+                *reinterpret_cast<uint2 *>(yp + n) = o;
+            }
+        }
+    }
+}
+
+// Zero rows [0, rows) of a tile's 256-column range (expert rows whose id is
+// out of range).
+template <class YRows>
+__device__ __forceinline__ void tile_store_zero(const YRows &yr, int rows, int n0, int N)
+{
+    for (int i = threadIdx.x; i < rows * (TL_TN / 4); i += TL_THREADS) {
+        const int r = i / (TL_TN / 4);
+        const int n = n0 + 4 * (i % (TL_TN / 4));
+        if (n < N)
+            *reinterpret_cast<uint2 *>(yr.row(r) + n) = uint2{0u, 0u};
+    }
+}
+
+// XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD takes a
+// contiguous run of the `tiles` tiles (N fastest), so its workgroups share
+// activation rows in that XCD's L2.  Returns -1 for workgroups beyond the run.
+__device__ __forceinline__ int xcd_tile(int tiles)
+{
+    const int per_xcd = (tiles + 7) >> 3;
+    const int b = blockIdx.x;
+    if ((b >> 3) >= per_xcd)
+        return -1;
+    const int t = (b & 7) * per_xcd + (b >> 3);
+    return t < tiles ? t : -1;
+}
+
+// Weight format policies -------------------------------------------------------
+
+// W4A16: packed codes qweight[N][K/8], scales[N][K/g] in DT, packed
+// zero-points qzeros[N/8][K/g] (or none: z = 8).  Each lane handles rows
+// n_nb = n0 + 64 wave + 32 nb + nl, which share n % 8, so one nibble shift of
+// the zero-point words serves both blocks.
+template <int DT, bool HAS_Z>
+struct FmtW4 {
+    static constexpr int NLOADS = HAS_Z ? 12 : 8;
+    struct Raw {
+        u32x4 w[2][2];
+        uint32_t s[2][2], z[2][2];
+    };
+    const uint8_t *wq, *ws, *wz;
+    uint32_t woff[2], soff[2], zoff[2];
+    int K, gshift, h, zsh;
+
+    __device__ FmtW4(const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
+                     int N, int K_, int gshift_, int n0, const TileLane &tl)
+    {
+        wq = reinterpret_cast<const uint8_t *>(qweight);
+        ws = reinterpret_cast<const uint8_t *>(scales);
+        wz = reinterpret_cast<const uint8_t *>(qzeros);
+        K = K_;
+        gshift = gshift_;
+        h = tl.h;
+        zsh = 4 * (tl.nl & 7);
+        const int G = K >> (5 + gshift);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int n = min(n0 + 64 * tl.wave + 32 * nb + tl.nl, N - 1);
+            woff[nb] = (uint32_t)n * (uint32_t)(K >> 1);
+            soff[nb] = (uint32_t)n * (uint32_t)G * 2u;
+            zoff[nb] = (uint32_t)(n >> 3) * (uint32_t)G * 4u;
+        }
+    }
+
+    __device__ __forceinline__ void load(int span, Raw &r) const
+    {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int k = span * TL_SPAN + 64 * h + 32 * hf;
+            const int kc = min(k, K - 32); // slice past K: clamped load, zeroed at dequant
+            const uint32_t kb = (uint32_t)kc >> 1;
+            const uint32_t grp = (uint32_t)(kc >> (5 + gshift));
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                r.w[nb][hf] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wq + woff[nb] + kb));
+                r.s[nb][hf] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + 2u * grp);
+                r.z[nb][hf] = HAS_Z ? *reinterpret_cast<const uint32_t *>(wz + zoff[nb] + 4u * grp)
+                                    : 0x88888888u;
+            }
+        }
+    }
+
+    __device__ __forceinline__ u32x4 dequant(const Raw &r, int nb, int st) const
+    {
+        const int hf = st >> 2;
+        const uint32_t z = (r.z[nb][hf] >> zsh) & 0xFu;
+        return w4_word_act8<DT>(r.w[nb][hf][st & 3], r.s[nb][hf], z);
+    }
+};
+
+// MXFP4: E2M1 codes w_fp4[N][K/2] (even k in the low nibble), E8M0 scales
+// w_scale[N][K/32]; needs K % 64 == 0 so a lane's two 32-wide slices share
+// one aligned 16-bit scale load.
+struct FmtFP4 {
+    static constexpr int NLOADS = 6;
+    struct Raw {
+        u32x4 w[2][2];
+        uint32_t s[2]; // E8M0 bytes of slices hf = 0 (low byte) and 1
+    };
+    const uint8_t *wq, *ws;
+    uint32_t woff[2], soff[2];
+    int K, h;
+
+    __device__ FmtFP4(const uint8_t *w_fp4, const uint8_t *w_scale, int N, int K_, int n0,
+                      const TileLane &tl)
+    {
+        wq = w_fp4;
+        ws = w_scale;
+        K = K_;
+        h = tl.h;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int n = min(n0 + 64 * tl.wave + 32 * nb + tl.nl, N - 1);
+            woff[nb] = (uint32_t)n * (uint32_t)(K >> 1);
+            soff[nb] = (uint32_t)n * (uint32_t)(K >> 5);
+        }
+    }
+
+    __device__ __forceinline__ void load(int span, Raw &r) const
+    {
+        const int k = min(span * TL_SPAN + 64 * h, K - 64); // past K: clamped, zeroed later
+        const uint32_t kb = (uint32_t)k >> 1;
+        const uint32_t kg = (uint32_t)k >> 5; // even
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                r.w[nb][hf] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4 *>(wq + woff[nb] + kb + 16u * hf));
+            r.s[nb] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + kg);
+        }
+    }
+
+    __device__ __forceinline__ u32x4 dequant(const Raw &r, int nb, int st) const
+    {
+        const int hf = st >> 2;
+        const float scale = e8m0_to_f32((r.s[nb] >> (8 * hf)) & 0xFFu);
+        return fp4_word_bf16x8(r.w[nb][hf][st & 3], scale);
+    }
+};
+
+} // namespace wob
