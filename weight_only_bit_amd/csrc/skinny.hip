@@ -51,8 +51,9 @@
 namespace wob {
 namespace {
 
-constexpr int SK_WAVES = 4;
-constexpr int SK_THREADS = 64 * SK_WAVES;
+constexpr int SK_WAVES = 4;     // waves per workgroup when K is split
+constexpr int SK_MAX_WAVES = 8; // largest workgroup
+constexpr int SK_MAX_THREADS = 64 * SK_MAX_WAVES;
 constexpr int SK_LDS_BUDGET = 64 * 1024;
 constexpr int SK_RING = 3; // chunk slots per row in the load ring
 
@@ -72,7 +73,7 @@ struct SkLds {
         sc = xsum + M * (K >> 5) * 4;
         zp = sc + ((octs_per_wg * 8 * G * 2 + 15) & ~15);
         red = zp + ((octs_per_wg * G * 4 + 15) & ~15);
-        total = red + SK_WAVES * 2 * M * 8 * 4; // up to two octets per wave
+        total = red + SK_MAX_WAVES * 2 * M * 8 * 4; // up to two octets per wave
     }
 };
 
@@ -82,7 +83,7 @@ template <int M, int RO>
 constexpr int sk_min_waves() { return RO == 2 ? 3 : (M <= 2 ? 4 : 2); }
 
 template <int DT, int M, int D, int GS, bool HAS_Z, int RO>
-__global__ __launch_bounds__(SK_THREADS, (sk_min_waves<M, RO>())) void w4a16_skinny_kernel(
+__global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16_skinny_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros,
     uint16_t *__restrict__ y, int N, int K, int ksplit)
@@ -92,7 +93,8 @@ __global__ __launch_bounds__(SK_THREADS, (sk_min_waves<M, RO>())) void w4a16_ski
     const int G = C >> GS; // groups per row
     const int RB = ((K + 255) >> 8) * 32;
     const int NO = N >> 3; // row octets
-    const int octs_per_wg = SK_WAVES / ksplit * RO;
+    const int nthr = blockDim.x; // 64 * waves of this workgroup
+    const int octs_per_wg = (nthr >> 6) / ksplit * RO;
     const SkLds L(M, K, G, octs_per_wg);
     u32x4 *xl = reinterpret_cast<u32x4 *>(smem + L.x);
     float *xsum = reinterpret_cast<float *>(smem + L.xsum);
@@ -112,20 +114,20 @@ __global__ __launch_bounds__(SK_THREADS, (sk_min_waves<M, RO>())) void w4a16_ski
     u32x4 xr[SK_XR];
 #pragma unroll
     for (int t = 0; t < SK_XR; ++t)
-        xr[t] = xs[min(tid + SK_THREADS * t, nvec - 1)];
+        xr[t] = xs[min(tid + nthr * t, nvec - 1)];
     const u32x4 *ss = reinterpret_cast<const u32x4 *>(scales + (size_t)oct0 * 8 * G);
     const int nsb = nocts * G; // 16-byte blocks of this workgroup's scales
     u32x4 sr[SK_SR];
 #pragma unroll
     for (int t = 0; t < SK_SR; ++t)
-        sr[t] = ss[min(tid + SK_THREADS * t, nsb - 1)];
+        sr[t] = ss[min(tid + nthr * t, nsb - 1)];
     const uint32_t *zs = HAS_Z ? qzeros + (size_t)oct0 * G : nullptr;
     const int nzw = nocts * G;
     uint32_t zr[SK_ZR];
     if constexpr (HAS_Z) {
 #pragma unroll
         for (int t = 0; t < SK_ZR; ++t)
-            zr[t] = zs[min(tid + SK_THREADS * t, nzw - 1)];
+            zr[t] = zs[min(tid + nthr * t, nzw - 1)];
     }
 
     // ---- this wave's work ----
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(SK_THREADS, (sk_min_waves<M, RO>())) void w4a16_ski
     const int rowblk = K >> 3;
 #pragma unroll
     for (int t = 0; t < SK_XR; ++t) {
-        const int i = tid + SK_THREADS * t;
+        const int i = tid + nthr * t;
         float bs = 0.f; // sum of this block's 8 values
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -187,21 +189,21 @@ __global__ __launch_bounds__(SK_THREADS, (sk_min_waves<M, RO>())) void w4a16_ski
         u32x4 *sd = reinterpret_cast<u32x4 *>(sl);
 #pragma unroll
         for (int t = 0; t < SK_SR; ++t) {
-            const int i = tid + SK_THREADS * t;
+            const int i = tid + nthr * t;
             if (i < nsb)
                 sd[i] = sr[t];
         }
         if constexpr (HAS_Z) {
 #pragma unroll
             for (int t = 0; t < SK_ZR; ++t) {
-                const int i = tid + SK_THREADS * t;
+                const int i = tid + nthr * t;
                 if (i < nzw)
                     zl[i] = zr[t];
             }
         }
     }
     // Rare large shapes: whatever did not fit the prologue registers.
-    for (int i = tid + SK_THREADS * SK_XR; i < nvec; i += SK_THREADS) {
+    for (int i = tid + nthr * SK_XR; i < nvec; i += nthr) {
         const u32x4 v = xs[i];
         float bs = 0.f;
 #pragma unroll
@@ -222,10 +224,10 @@ __global__ __launch_bounds__(SK_THREADS, (sk_min_waves<M, RO>())) void w4a16_ski
         if (wi == 0)
             xsum[m * C + j] = bs;
     }
-    for (int i = tid + SK_THREADS * SK_SR; i < nsb; i += SK_THREADS)
+    for (int i = tid + nthr * SK_SR; i < nsb; i += nthr)
         reinterpret_cast<u32x4 *>(sl)[i] = ss[i];
     if constexpr (HAS_Z) {
-        for (int i = tid + SK_THREADS * SK_ZR; i < nzw; i += SK_THREADS)
+        for (int i = tid + nthr * SK_ZR; i < nzw; i += nthr)
             zl[i] = zs[i];
     }
     __syncthreads();
@@ -374,63 +376,92 @@ __global__ __launch_bounds__(SK_THREADS, (sk_min_waves<M, RO>())) void w4a16_ski
     }
 }
 
-// Octets per wave: two when there are enough rows to keep every CU busy.
-int ro_for(int M, int N) { return (M <= 2 && N / 8 >= 4096) ? 2 : 1; }
+// Launch shape: RO octets per wave, `waves` waves per workgroup, K split
+// `ksplit` ways across the waves of a workgroup.
+struct SkCfg {
+    int ro, waves, ksplit;
+};
 
-int ksplit_for(int N, int K)
+// Compute units of gfx950 (8 XCDs x 32): workgroups are spread over them.
+constexpr int SK_CUS = 256;
+
+SkCfg sk_config(int M, int N, int K)
 {
-    // Split K across waves of a workgroup while there are few row octets,
-    // keeping at least two chunks per lane.
     const int octs = N / 8;
     const int C = K / 32;
+    // Enough row octets to fill the chip without splitting K: pick the
+    // octets-per-wave and workgroup size that spread the work most evenly over
+    // the compute units (each CU streams at a bounded rate, so the CU with the
+    // most workgroups sets the kernel time; measured on the decode shape, the
+    // CUs holding one workgroup more than the others finished last).
+    if (octs >= 16 * SK_CUS) {
+        SkCfg best{1, SK_WAVES, 1};
+        double best_eff = -1.0;
+        for (int ro = 1; ro <= (M <= 2 ? 2 : 1); ++ro) {
+            const int units = (octs + ro - 1) / ro;
+            for (int w = SK_MAX_WAVES; w >= 2; --w) {
+                const int wgs = (units + w - 1) / w;
+                const int per_cu = (wgs + SK_CUS - 1) / SK_CUS;
+                const double eff = (double)octs / ((double)SK_CUS * per_cu * w * ro);
+                if (eff > best_eff + 1e-9) {
+                    best_eff = eff;
+                    best = SkCfg{ro, w, 1};
+                }
+            }
+        }
+        return best;
+    }
+    // Few row octets: split K across the waves of a workgroup, keeping at
+    // least two chunks per lane.
     int ksplit = 1;
     while (ksplit < SK_WAVES && octs * ksplit < 4096 && C >= 16 * ksplit * 2)
         ksplit *= 2;
-    return ksplit;
+    return SkCfg{1, SK_WAVES, ksplit};
 }
 
 int lds_bytes(int M, int N, int K, int g)
 {
-    return SkLds(M, K, K / g, SK_WAVES / ksplit_for(N, K) * ro_for(M, N)).total;
+    const SkCfg c = sk_config(M, N, K);
+    return SkLds(M, K, K / g, c.waves / c.ksplit * c.ro).total;
 }
 
 template <int DT, int M, int GS, int RO>
-hipError_t launch_r(const W4Args &a, int grid, int ksplit, size_t lds, hipStream_t stream)
+hipError_t launch_r(const W4Args &a, const SkCfg &c, size_t lds, hipStream_t stream)
 {
+    const int octs_per_wg = c.waves / c.ksplit * RO;
+    const int grid = (a.N / 8 + octs_per_wg - 1) / octs_per_wg;
     if (a.qzeros)
         hipLaunchKernelGGL((w4a16_skinny_kernel<DT, M, SK_RING, GS, true, RO>), dim3(grid),
-                           dim3(SK_THREADS), lds, stream, static_cast<const uint16_t *>(a.x),
+                           dim3(64 * c.waves), lds, stream, static_cast<const uint16_t *>(a.x),
                            a.qweight, static_cast<const uint16_t *>(a.scales), a.qzeros,
-                           static_cast<uint16_t *>(a.y), a.N, a.K, ksplit);
+                           static_cast<uint16_t *>(a.y), a.N, a.K, c.ksplit);
     else
         hipLaunchKernelGGL((w4a16_skinny_kernel<DT, M, SK_RING, GS, false, RO>), dim3(grid),
-                           dim3(SK_THREADS), lds, stream, static_cast<const uint16_t *>(a.x),
+                           dim3(64 * c.waves), lds, stream, static_cast<const uint16_t *>(a.x),
                            a.qweight, static_cast<const uint16_t *>(a.scales), a.qzeros,
-                           static_cast<uint16_t *>(a.y), a.N, a.K, ksplit);
+                           static_cast<uint16_t *>(a.y), a.N, a.K, c.ksplit);
     return hipGetLastError();
 }
 
 template <int DT, int M, int GS>
-hipError_t launch_g(const W4Args &a, int grid, int ksplit, size_t lds, hipStream_t stream)
+hipError_t launch_g(const W4Args &a, const SkCfg &c, size_t lds, hipStream_t stream)
 {
     if constexpr (M <= 2) {
-        if (ro_for(M, a.N) == 2)
-            return launch_r<DT, M, GS, 2>(a, grid, ksplit, lds, stream);
+        if (c.ro == 2)
+            return launch_r<DT, M, GS, 2>(a, c, lds, stream);
     }
-    return launch_r<DT, M, GS, 1>(a, grid, ksplit, lds, stream);
+    return launch_r<DT, M, GS, 1>(a, c, lds, stream);
 }
 
 template <int DT, int M>
 hipError_t launch_m(const W4Args &a, hipStream_t stream)
 {
-    const int ksplit = ksplit_for(a.N, a.K);
-    const int octs_per_wg = SK_WAVES / ksplit * ro_for(M, a.N);
-    const int grid = (a.N / 8 + octs_per_wg - 1) / octs_per_wg;
+    const SkCfg c = sk_config(M, a.N, a.K);
     const size_t lds = (size_t)lds_bytes(M, a.N, a.K, a.g);
     switch (a.g) {
-    case 32: return launch_g<DT, M, 0>(a, grid, ksplit, lds, stream);
-    case 64: return launch_g<DT, M, 1>(a, grid, ksplit, lds, stream);
-    default: return launch_g<DT, M, 2>(a, grid, ksplit, lds, stream);
+    case 32: return launch_g<DT, M, 0>(a, c, lds, stream);
+    case 64: return launch_g<DT, M, 1>(a, c, lds, stream);
+    default: return launch_g<DT, M, 2>(a, c, lds, stream);
     }
 }
 

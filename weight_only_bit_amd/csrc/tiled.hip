@@ -118,7 +118,7 @@ __device__ __forceinline__ void run_tile(const Fmt &fmt, const ContigRows &rws, 
                                          int K, int N, int n0, uint8_t *smem, const TileLane &tl)
 {
     float16_t acc[2][MB];
-    tile_mainloop<DT, MB>(fmt, rws, xbase, K, smem, tl, acc);
+    tile_mainloop<DT, MB>(fmt, rws, xbase, K, n0, N, smem, tl, acc);
     tile_store<DT, MB>(acc, rws, rws.rows, n0, N, tl);
 }
 

@@ -31,21 +31,32 @@
 //    (32 rows x one block each) bank-conflict free.  Rows come from a per-lane
 //    byte offset supplied by the caller, so the same copy serves contiguous
 //    rows and gathered (routed) rows.
+//  * The packed codes of the 256 weight rows (64 bytes per row per span) are
+//    copied into LDS the same way, 16 rows per wave instruction, so each
+//    instruction reads sixteen contiguous 64-byte row segments instead of
+//    scattering 16-byte pieces of 32 rows (measured: the scattered per-lane
+//    code loads cost more than a fifth of the kernel).  A lane reads back its
+//    two rows' 32 bytes per span with four ds_read_b128; LDS row R keeps its
+//    16-byte piece p at position p ^ ((R >> 2) & 3), which makes those reads
+//    bank-conflict free.
 //  * Software pipeline: within a span the loop runs over the 8 MFMA steps;
 //    each step dequantizes the two weight words it needs (one per 32-row
 //    block) and issues its 2 x MB MFMAs, while the next step's activation
-//    operands are read from LDS and its two words are dequantized.  The raw
-//    packed weights are double buffered in registers and loaded a whole span
-//    ahead; the next span's activation tile streams into the other LDS buffer.
+//    operands are read from LDS and its two words are dequantized.  The
+//    per-row scales and zero-points are double buffered in registers and
+//    loaded a whole span ahead; the next span's activation and code tiles
+//    stream into the other LDS buffers.
 //  * Tails: weight rows past the matrix are clamped to valid addresses and
 //    never stored; activation rows past the tile's row count are clamped to a
 //    valid row and never stored; a 32-wide K slice past K gets zero weights.
 //
-// Weight formats plug in as a policy with:
-//    struct Raw;                          raw loads of one span for one lane
-//    static constexpr int NLOADS;         vector-memory operations per load()
-//    void load(int span, Raw &r) const;   issue this lane's loads of a span
-//    u32x4 dequant(const Raw &, int nb, int st) const;  8 operand values
+// Weight formats (4-bit codes, K/2 bytes per row, at `wq`) plug in as a
+// policy with:
+//    const uint8_t *wq;                   codes of row 0 of the matrix
+//    struct Meta;                         a lane's scales / zero-points of a span
+//    static constexpr int NLOADS;         vector-memory operations per load_meta()
+//    void load_meta(int span, Meta &m) const;
+//    u32x4 dequant(uint32_t word, const Meta &m, int nb, int st) const;
 #pragma once
 
 #include "wob_device.hpp"
@@ -63,7 +74,11 @@ constexpr int TL_ROWB = 256;         // LDS bytes per activation row of a span
 constexpr int TL_MB_MAX = 8;         // largest tile: 256 activation rows
 
 // LDS bytes of a tile with up to mb_max 32-row blocks (two span buffers).
-__host__ __device__ constexpr int tile_lds_bytes(int mb_max) { return 2 * 32 * mb_max * TL_ROWB; }
+constexpr int TL_WBUF = TL_TN * 64; // LDS bytes of one span's code tile
+__host__ __device__ constexpr int tile_lds_bytes(int mb_max)
+{
+    return 2 * 32 * mb_max * TL_ROWB + 2 * TL_WBUF;
+}
 
 // s_waitcnt that waits until at most `n` vector-memory operations are
 // outstanding (expcnt and lgkmcnt left alone; gfx9 encoding).
@@ -144,12 +159,34 @@ struct TileLane {
 // the accumulators in `acc`.  `Fmt` holds this lane's weight addressing.
 template <int DT, int MB, class Fmt, class XRows>
 __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
-                                              const uint8_t *xbase, int K, uint8_t *smem,
-                                              const TileLane &tl, float16_t (&acc)[2][MB])
+                                              const uint8_t *xbase, int K, int n0, int N,
+                                              uint8_t *smem, const TileLane &tl,
+                                              float16_t (&acc)[2][MB])
 {
     constexpr int TM = 32 * MB;
     const int S = (K + TL_SPAN - 1) / TL_SPAN;
     const uint32_t lds0 = (uint32_t)(size_t)(lds_ptr_t *)smem;
+    const uint32_t wlds0 = lds0 + (uint32_t)(2 * TM * TL_ROWB);
+    const uint8_t *wsm = smem + 2 * TM * TL_ROWB;
+
+    // Code tile DMA: 256 rows x 64 bytes per span, 16 rows (1 KB) per wave
+    // instruction, instructions 4 w .. 4 w + 3 for wave w.  Lane L writes row
+    // L / 4 of the instruction's 16 at position L % 4, so it copies piece
+    // (L % 4) ^ (L / 16) of that row.  Rows past N are clamped (never stored);
+    // pieces past the end of a row are clamped inside it (zeroed at dequant).
+    const uint32_t rowb = (uint32_t)K >> 1;
+    uint32_t crow[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+        crow[jj] = (uint32_t)min(n0 + 16 * (4 * tl.wave + jj) + (tl.lane >> 2), N - 1) * rowb;
+    const uint32_t cpiece = 16u * (uint32_t)((tl.lane & 3) ^ (tl.lane >> 4));
+    auto issue_w = [&](int span, int buf) __attribute__((always_inline)) {
+        const uint32_t kb = min((uint32_t)span * 64u + cpiece, rowb - 16u);
+        const uint32_t dst = wlds0 + (uint32_t)(buf * TL_WBUF + 4 * tl.wave * 1024);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            lds_dma16(fmt.wq, crow[jj] + kb, __builtin_amdgcn_readfirstlane(dst + 1024u * jj));
+    };
 
     // Activation tile DMA: TM rows x 16 blocks per span, 1 KB per wave
     // instruction.  Instruction i of wave w fills LDS rows 16 i + 4 w .. +3;
@@ -173,22 +210,36 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
             for (int e = 0; e < 16; ++e)
                 acc[nb][mb][e] = 0.f;
 
-    // Raw weights double buffered: rA / rB alternate between "this span"
-    // (complete) and "next span" (loads in flight).
-    typename Fmt::Raw rA, rB;
-    fmt.load(0, rA);
-    fmt.load(min(1, S - 1), rB);
+    // Scales / zero-points double buffered: mA / mB alternate between "this
+    // span" (complete) and "next span" (loads in flight).
+    typename Fmt::Meta mA, mB;
+    fmt.load_meta(0, mA);
+    fmt.load_meta(min(1, S - 1), mB);
     issue_x(0, 0);
+    issue_w(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     barrier_only();
 
-    // One span: MFMAs on LDS buffer span & 1 with the weights in `cur`.  At
-    // entry the next span's raw weights (the other buffer) have landed or are
-    // in flight; this span's `cur` is refilled for span + 2 once consumed.
-    auto run_span = [&](int span, typename Fmt::Raw &cur) __attribute__((always_inline)) {
+    // One span: MFMAs on LDS buffers span & 1 with the scales in `cur`.  At
+    // entry the next span's scales (the other buffer) have landed or are in
+    // flight; this span's `cur` is refilled for span + 2 once consumed.
+    auto run_span = [&](int span, typename Fmt::Meta &cur) __attribute__((always_inline)) {
         const int buf = span & 1;
         issue_x(min(span + 1, S - 1), buf ^ 1);
+        issue_w(min(span + 1, S - 1), buf ^ 1);
         const uint8_t *xb = smem + (size_t)buf * TM * TL_ROWB;
+        // This lane's packed codes of the span: rows 64 w + 32 nb + nl, pieces
+        // 2 h + hf (k = 64 h + 32 hf .. +31 of the span).
+        const uint8_t *wb = wsm + buf * TL_WBUF;
+        u32x4 cw[2][2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int R = 64 * tl.wave + 32 * nb + tl.nl;
+                const int pos = (2 * tl.h + hf) ^ ((tl.nl >> 2) & 3);
+                cw[nb][hf] = *reinterpret_cast<const u32x4 *>(wb + R * 64 + 16 * pos);
+            }
         // Activation operand of block mb, step st: 32 rows (nl), 16-byte
         // block 8h + st of the span.
         auto read_x = [&](int mb, int st) __attribute__((always_inline)) {
@@ -198,7 +249,7 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
         };
         const bool ktail = span * TL_SPAN + TL_SPAN > K;
         auto dq = [&](int nb, int st) __attribute__((always_inline)) {
-            u32x4 v = fmt.dequant(cur, nb, st);
+            u32x4 v = fmt.dequant(cw[nb][st >> 2][st & 3], cur, nb, st);
             // only a span that crosses K (uniform test) zeroes the slices past K
             if (ktail && span * TL_SPAN + 64 * tl.h + 32 * (st >> 2) >= K)
                 v = u32x4{0, 0, 0, 0};
@@ -237,24 +288,24 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
             }
         }
         // `cur` is consumed: refill it for span + 2 (clamped, so the wait
-        // counts stay exact), then the barrier that publishes the next tile:
-        // wait for everything but that refill (next activation tile + the
-        // next span's weights).
-        fmt.load(min(span + 2, S - 1), cur);
+        // counts stay exact), then the barrier that publishes the next tiles:
+        // wait for everything but that refill (next activation and code
+        // tiles + the next span's scales).
+        fmt.load_meta(min(span + 2, S - 1), cur);
         wait_vmcnt<Fmt::NLOADS>();
         barrier_only();
     };
 
     int span = 0;
     for (; span + 1 < S; span += 2) {
-        run_span(span, rA);
-        run_span(span + 1, rB);
+        run_span(span, mA);
+        run_span(span + 1, mB);
     }
     if (span < S)
-        run_span(span, rA);
-    // Only the last (clamped, duplicate) weight refill can still be in flight
+        run_span(span, mA);
+    // Only the last (clamped, duplicate) scale refill can still be in flight
     // here; it targets registers, which the compiler's own wait counts cover.
-    // Every activation copy into LDS has been waited for.
+    // Every copy into LDS has been waited for.
 }
 
 // Store one tile's accumulators: lane holds D[n = 8 g4 + 4 h + j][m = nl] of
@@ -321,13 +372,12 @@ __device__ __forceinline__ int xcd_tile(int tiles)
 // the zero-point words serves both blocks.
 template <int DT, bool HAS_Z>
 struct FmtW4 {
-    static constexpr int NLOADS = HAS_Z ? 12 : 8;
-    struct Raw {
-        u32x4 w[2][2];
+    static constexpr int NLOADS = HAS_Z ? 8 : 4;
+    struct Meta {
         uint32_t s[2][2], z[2][2];
     };
     const uint8_t *wq, *ws, *wz;
-    uint32_t woff[2], soff[2], zoff[2];
+    uint32_t soff[2], zoff[2];
     int K, gshift, h, zsh;
 
     __device__ FmtW4(const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
@@ -344,35 +394,32 @@ struct FmtW4 {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             const int n = min(n0 + 64 * tl.wave + 32 * nb + tl.nl, N - 1);
-            woff[nb] = (uint32_t)n * (uint32_t)(K >> 1);
             soff[nb] = (uint32_t)n * (uint32_t)G * 2u;
             zoff[nb] = (uint32_t)(n >> 3) * (uint32_t)G * 4u;
         }
     }
 
-    __device__ __forceinline__ void load(int span, Raw &r) const
+    __device__ __forceinline__ void load_meta(int span, Meta &m) const
     {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int k = span * TL_SPAN + 64 * h + 32 * hf;
             const int kc = min(k, K - 32); // slice past K: clamped load, zeroed at dequant
-            const uint32_t kb = (uint32_t)kc >> 1;
             const uint32_t grp = (uint32_t)(kc >> (5 + gshift));
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
-                r.w[nb][hf] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wq + woff[nb] + kb));
-                r.s[nb][hf] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + 2u * grp);
-                r.z[nb][hf] = HAS_Z ? *reinterpret_cast<const uint32_t *>(wz + zoff[nb] + 4u * grp)
+                m.s[nb][hf] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + 2u * grp);
+                m.z[nb][hf] = HAS_Z ? *reinterpret_cast<const uint32_t *>(wz + zoff[nb] + 4u * grp)
                                     : 0x88888888u;
             }
         }
     }
 
-    __device__ __forceinline__ u32x4 dequant(const Raw &r, int nb, int st) const
+    __device__ __forceinline__ u32x4 dequant(uint32_t word, const Meta &m, int nb, int st) const
     {
         const int hf = st >> 2;
-        const uint32_t z = (r.z[nb][hf] >> zsh) & 0xFu;
-        return w4_word_act8<DT>(r.w[nb][hf][st & 3], r.s[nb][hf], z);
+        const uint32_t z = (m.z[nb][hf] >> zsh) & 0xFu;
+        return w4_word_act8<DT>(word, m.s[nb][hf], z);
     }
 };
 
@@ -380,13 +427,12 @@ struct FmtW4 {
 // w_scale[N][K/32]; needs K % 64 == 0 so a lane's two 32-wide slices share
 // one aligned 16-bit scale load.
 struct FmtFP4 {
-    static constexpr int NLOADS = 6;
-    struct Raw {
-        u32x4 w[2][2];
+    static constexpr int NLOADS = 2;
+    struct Meta {
         uint32_t s[2]; // E8M0 bytes of slices hf = 0 (low byte) and 1
     };
     const uint8_t *wq, *ws;
-    uint32_t woff[2], soff[2];
+    uint32_t soff[2];
     int K, h;
 
     __device__ FmtFP4(const uint8_t *w_fp4, const uint8_t *w_scale, int N, int K_, int n0,
@@ -399,31 +445,24 @@ struct FmtFP4 {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             const int n = min(n0 + 64 * tl.wave + 32 * nb + tl.nl, N - 1);
-            woff[nb] = (uint32_t)n * (uint32_t)(K >> 1);
             soff[nb] = (uint32_t)n * (uint32_t)(K >> 5);
         }
     }
 
-    __device__ __forceinline__ void load(int span, Raw &r) const
+    __device__ __forceinline__ void load_meta(int span, Meta &m) const
     {
         const int k = min(span * TL_SPAN + 64 * h, K - 64); // past K: clamped, zeroed later
-        const uint32_t kb = (uint32_t)k >> 1;
-        const uint32_t kg = (uint32_t)k >> 5; // even
+        const uint32_t kg = (uint32_t)k >> 5;               // even
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-                r.w[nb][hf] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4 *>(wq + woff[nb] + kb + 16u * hf));
-            r.s[nb] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + kg);
-        }
+        for (int nb = 0; nb < 2; ++nb)
+            m.s[nb] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + kg);
     }
 
-    __device__ __forceinline__ u32x4 dequant(const Raw &r, int nb, int st) const
+    __device__ __forceinline__ u32x4 dequant(uint32_t word, const Meta &m, int nb, int st) const
     {
         const int hf = st >> 2;
-        const float scale = e8m0_to_f32((r.s[nb] >> (8 * hf)) & 0xFFu);
-        return fp4_word_bf16x8(r.w[nb][hf][st & 3], scale);
+        const float scale = e8m0_to_f32((m.s[nb] >> (8 * hf)) & 0xFFu);
+        return fp4_word_bf16x8(word, scale);
     }
 };
 
