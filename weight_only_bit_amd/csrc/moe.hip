@@ -169,7 +169,7 @@ __device__ __forceinline__ void moe_run(const FmtFP4 &fmt, const int32_t *pairs,
     float16_t acc[2][MB];
     tile_mainloop<DT_BF16, MB>(fmt, g, reinterpret_cast<const uint8_t *>(x), K, n0, N, smem, tl,
                                acc);
-    tile_store<DT_BF16, MB>(acc, g, rows, n0, N, tl);
+    tile_store<DT_BF16, MB>(acc, g, rows, n0, N, tl, smem);
 }
 
 template <int MB>

@@ -119,7 +119,7 @@ __device__ __forceinline__ void run_tile(const Fmt &fmt, const ContigRows &rws, 
 {
     float16_t acc[2][MB];
     tile_mainloop<DT, MB>(fmt, rws, xbase, K, n0, N, smem, tl, acc);
-    tile_store<DT, MB>(acc, rws, rws.rows, n0, N, tl);
+    tile_store<DT, MB>(acc, rws, rws.rows, n0, N, tl, smem);
 }
 
 // Runs the tile with the smallest block count that covers `rows`.

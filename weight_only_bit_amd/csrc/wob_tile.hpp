@@ -308,33 +308,46 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
     // Every copy into LDS has been waited for.
 }
 
-// Store one tile's accumulators: lane holds D[n = 8 g4 + 4 h + j][m = nl] of
-// block (nb, mb) in register 4 g4 + j.  `yrow(r)` returns the output row
-// pointer of tile row r, called only for r < rows.
+// Store one tile's accumulators through LDS, so that every global store
+// instruction writes whole 512-byte row segments of y (measured: storing the
+// accumulator layout directly, 8 bytes per lane across 32 rows, took about a
+// twelfth of the prefill kernel).  Lane holds D[n = 8 g4 + 4 h + j][m = nl] of
+// block (nb, mb) in register 4 g4 + j; the tile is staged as TM rows of 256
+// activation-dtype values (row stride padded by 16 bytes against bank
+// conflicts) in the LDS the main loop has released.  `yr.row(r)` returns the
+// output row pointer of tile row r, called only for r < rows.
 template <int DT, int MB, class YRows>
 __device__ __forceinline__ void tile_store(const float16_t (&acc)[2][MB], const YRows &yr, int rows,
-                                          int n0, int N, const TileLane &tl)
+                                          int n0, int N, const TileLane &tl, uint8_t *smem)
 {
+    constexpr int TM = 32 * MB;
+    constexpr int RS = TL_TN * 2 + 16; // LDS bytes per staged row
+    static_assert(TM * RS <= 2 * TM * TL_ROWB + 2 * TL_WBUF, "staging fits the tile's LDS");
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        const int r = 32 * mb + tl.nl;
-        if (r >= rows)
-            continue;
-        uint16_t *yp = yr.row(r);
+        const int m = 32 * mb + tl.nl;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                const int n = n0 + 64 * tl.wave + 32 * nb + 8 * g4 + 4 * tl.h;
-                if (n >= N)
-                    continue;
+                const int c = 64 * tl.wave + 32 * nb + 8 * g4 + 4 * tl.h;
                 const float16_t &v = acc[nb][mb];
                 uint2 o;
                 o.x = f32x2_to_act2<DT>(v[4 * g4 + 0], v[4 * g4 + 1]);
                 o.y = f32x2_to_act2<DT>(v[4 * g4 + 2], v[4 * g4 + 3]);
-                *reinterpret_cast<uint2 *>(yp + n) = o;
+                *reinterpret_cast<uint2 *>(smem + m * RS + 2 * c) = o;
             }
         }
+    }
+    __syncthreads();
+    // 32 chunks of 16 bytes (8 values) per staged row; N % 8 == 0, so a chunk
+    // is either wholly inside the matrix or wholly past it.
+    for (int i = threadIdx.x; i < TM * 32; i += TL_THREADS) {
+        const int r = i >> 5, c = i & 31;
+        const int n = n0 + 8 * c;
+        if (r < rows && n < N)
+            *reinterpret_cast<u32x4 *>(yr.row(r) + n) =
+                *reinterpret_cast<const u32x4 *>(smem + r * RS + 16 * c);
     }
 }
 
