@@ -66,6 +66,10 @@ extern "C" {
 #define WOB_U4X8_I32 2 /* eight 4-bit values packed in an int32 */
 #define WOB_F32 3
 
+/* MoE stage-1 activation for mxfp4_moe_gemm_act. */
+#define WOB_ACT_NONE 0     /* pre-activation output [T][topk][N] */
+#define WOB_ACT_SILU_MUL 1 /* silu(gate) * up: output [T][topk][N/2] */
+
 /* Kernel path selection for w4a16_gemm_ex. */
 #define WOB_PATH_AUTO 0   /* M <= 8 (and X fits the skinny kernel's LDS) -> skinny, else tiled */
 #define WOB_PATH_SKINNY 1 /* split-K GEMV; requires M <= 8 */
@@ -144,6 +148,25 @@ size_t mxfp4_moe_gemm_workspace_size(int64_t T, int64_t topk, int64_t E);
 int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
                    const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E, int64_t N,
                    int64_t K, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * MoE stage 1 with its activation fused into the store.  act == WOB_ACT_NONE
+ * is exactly mxfp4_moe_gemm.  act == WOB_ACT_SILU_MUL reads the N rows of each
+ * expert's W1 as a gate half (rows 0 .. N/2-1) and an up half (rows N/2 ..
+ * N-1) and writes
+ *   y[t][s][n] = silu(g) * u,  g = pre[t][s][n], u = pre[t][s][N/2 + n],
+ *   silu(v) = v / (1 + e^-v),  n < N/2,
+ * into y [T][topk][N/2] bf16, where pre is the mxfp4_moe_gemm output (kept in
+ * fp32, never written).  Source: MXFP4 page above, summary and Test (the
+ * stage-1 kernel's silu activation; its gate/up split of W1 is this library's
+ * reading).  Needs N % 32 == 0 for WOB_ACT_SILU_MUL; otherwise the same rules,
+ * workspace and error behaviour as mxfp4_moe_gemm (an unknown act gives
+ * WOB_INVALID_ARG).
+ */
+int mxfp4_moe_gemm_act(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
+                       const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E,
+                       int64_t N, int64_t K, int act, void *workspace, size_t workspace_bytes,
+                       void *stream);
 
 /*
  * Dequantization probes: run the same device dequantization helpers the GEMM

@@ -212,6 +212,16 @@ def mxfp4_moe_gemm(x, ids, w_fp4, w_scale, T, topk, E, N, K):
     return y
 
 
+def silu_mul(ypre):
+    """Stage-1 activation of pre-activation rows [..., N]: silu(gate) * up -> [..., N/2]."""
+    y = _c(ypre, np.float64)
+    N = y.shape[-1]
+    rows = y.size // N
+    out = np.empty(y.shape[:-1] + (N // 2,), np.float64)
+    _load().oracle_silu_mul(_p(y), ctypes.c_int64(rows), ctypes.c_int64(N), _p(out))
+    return out
+
+
 def mxfp4_moe_gemm_sampled(x, ids, w_fp4, w_scale, topk, E, N, K, ts, slots, ns):
     xx = _c(x, np.uint16)
     ii = _c(ids, np.int32)

@@ -18,6 +18,8 @@
  *       -- summary, Technical Details.
  *  [P3] "qsa_prompt_attn: Q4_0 KV on tensor cores (mode 4)" (strata pull
  *       request 452) -- section What (offset-8 codes).
+ *  [P4] also names the stage-1 activation (silu); its gate/up split of W1 is
+ *       read here as gate = first half of the rows, up = second half.
  *  Outside definitions: IEEE 754-2008 binary16; the bfloat16 format (top 16
  *  bits of binary32); OCP Microscaling Formats (MX) v1.0, E2M1 element and
  *  E8M0 scale.
@@ -30,7 +32,9 @@
  *  - scales share the activation dtype; a missing zero-point tensor means the
  *    symmetric code offset 8 (as the offset-8 codes of [P3] What);
  *  - MXFP4 bytes hold the even-k element in the low nibble;
- *  - an expert id outside [0, E) yields an all-zero output row.
+ *  - an expert id outside [0, E) yields an all-zero output row;
+ *  - the stage-1 activation is silu(gate) * up, silu(v) = v / (1 + e^-v),
+ *    with gate the first N/2 outputs of a row and up the last N/2.
  *
  * Parity pins (tests/test_oracle_*.py): brute-force integer matmul, nibble
  * pack/unpack round trip with hand words, dense fp64/fp32 GEMM on the oracle's
@@ -370,4 +374,21 @@ void oracle_mxfp4_moe_gemm_sampled(const uint16_t *x, const int32_t *ids, const 
                           ns[i], w_row);
         out[i] = dot_row(x, DT_BF16, ts[i], K, w_row);
     }
+}
+
+/*
+ * MoE stage-1 activation on pre-activation rows ypre[rows][N]: the first N/2
+ * values of a row are the gate half, the last N/2 the up half, and
+ * out[r][n] = silu(gate[n]) * up[n] with silu(v) = v / (1 + e^-v), evaluated
+ * in binary64.
+ */
+void oracle_silu_mul(const double *ypre, int64_t rows, int64_t N, double *out)
+{
+    int64_t I = N / 2;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t n = 0; n < I; ++n) {
+            double g = ypre[r * N + n];
+            double u = ypre[r * N + I + n];
+            out[r * I + n] = g / (1.0 + exp(-g)) * u;
+        }
 }

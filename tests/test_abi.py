@@ -105,6 +105,9 @@ def test_moe_checks(L):
     assert call(K=96) == L.INVALID_ARG  # the K tile is 64 wide
     assert call(N=24) == L.INVALID_ARG
     assert call(T=1 << 21, K=1 << 11) == L.INVALID_ARG  # x past 32-bit byte offsets
+    act = lambda a, N=32: L.lib().mxfp4_moe_gemm_act(p, p, p, p, p, 4, 4, 32, N, 64, a, p, need, None)
+    assert act(2) == L.INVALID_ARG          # unknown activation
+    assert act(1, N=48) == L.INVALID_ARG    # silu(gate) * up needs N % 32 == 0
     assert call(ws=0) == L.INVALID_ARG
     assert call(T=0) == L.OK
 

@@ -134,3 +134,70 @@ def test_config_moe_stage1_full_size(wob, oracle):
     # the bound takes the sampled outputs' max|y_ref|: no looser than the global one
     ok, err, bound = oracle.tolerance_ok(y[ts, ss, ns], yref)
     assert ok, (err, bound)
+
+
+# --- fused stage-1 activation: silu(gate) * up -------------------------------------
+
+def _run_act(wob, d, ids=None):
+    torch = torch_mod()
+    T, topk, N = d["T"], d["topk"], d["N"]
+    ids = d["ids"] if ids is None else ids
+    out = torch.empty((T * topk + 2, N // 2), dtype=torch.bfloat16, device="cuda")
+    out.fill_(float("nan"))
+    y = out[1:T * topk + 1].view(T, topk, N // 2)
+    x = dev(d["x"].view(np.int16)).view(torch.bfloat16)
+    wob.mxfp4_moe_gemm(x, dev(ids), dev(d["w_fp4"]), dev(d["w_scale"]), out=y,
+                       act=wob.ACT_SILU_MUL)
+    torch.cuda.synchronize()
+    bits = host_bits(out)
+    assert np.all(is_nan_bits(bits[0], wl.BF16)) and np.all(is_nan_bits(bits[-1], wl.BF16))
+    return bits[1:-1].reshape(T, topk, N // 2)
+
+
+@pytest.mark.parametrize("T,E,topk,N,K", [(64, 8, 2, 512, 256), (37, 4, 3, 416, 192),
+                                          (200, 16, 4, 5760, 640), (5, 32, 4, 32, 64)])
+def test_moe_silu_mul_parity(wob, oracle, T, E, topk, N, K):
+    d = wl.moe_inputs(T, E, topk, N, K, seed=T + N + 1)
+    ids = d["ids"].copy()
+    ids[0, 0] = -1  # out-of-range id: zero row
+    pre = oracle.mxfp4_moe_gemm(d["x"], ids, d["w_fp4"], d["w_scale"], T, topk, E, N, K)
+    ref = oracle.silu_mul(pre)
+    ybits = _run_act(wob, d, ids)
+    ok, err, bound = oracle.tolerance_ok(oracle.bf16_decode(ybits), ref)
+    assert ok, f"max err {err} > bound {bound}"
+    assert np.all(ybits[0, 0] == 0)
+
+
+@pytest.mark.parametrize("rows_per_expert", [16, 100, 257])
+def test_moe_silu_mul_tile_heights(wob, oracle, rows_per_expert):
+    E = 3
+    T = E * rows_per_expert
+    d = wl.moe_inputs(T, E, 1, 288, 320, seed=rows_per_expert + 5)
+    ids = (np.arange(T) % E).astype(np.int32).reshape(T, 1)
+    pre = oracle.mxfp4_moe_gemm(d["x"], ids, d["w_fp4"], d["w_scale"], T, 1, E, 288, 320)
+    ok, err, bound = oracle.tolerance_ok(oracle.bf16_decode(_run_act(wob, d, ids)),
+                                         oracle.silu_mul(pre))
+    assert ok, f"max err {err} > bound {bound}"
+
+
+def test_config_moe_stage1_silu_mul_full_size(wob, oracle):
+    """The full MoE shape with the fused activation: all outputs finite, 2000
+    sampled outputs against the oracle's silu(gate) * up of sampled gate and
+    up pre-activations."""
+    d = wl.BY_KEY["moe_stage1"].make()
+    ybits = _run_act(wob, d)
+    y = oracle.bf16_decode(ybits)
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(1)
+    T, topk, N = d["T"], d["topk"], d["N"]
+    I = N // 2
+    ts = rng.integers(0, T, 2000)
+    ss = rng.integers(0, topk, 2000)
+    ns = rng.integers(0, I, 2000)
+    ns[:2] = [0, I - 1]
+    args = (d["x"], d["ids"], d["w_fp4"], d["w_scale"], topk, d["E"], N, d["K"])
+    gate = oracle.mxfp4_moe_gemm_sampled(*args, ts, ss, ns)
+    up = oracle.mxfp4_moe_gemm_sampled(*args, ts, ss, ns + I)
+    ref = oracle.silu_mul(np.stack([gate, up], axis=-1))[..., 0]
+    ok, err, bound = oracle.tolerance_ok(y[ts, ss, ns], ref)
+    assert ok, (err, bound)

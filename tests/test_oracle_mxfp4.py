@@ -108,3 +108,39 @@ def test_parity_rule_catches_swapped_fp4_nibbles(oracle):
     y_bad = oracle.mxfp4_moe_gemm(d["x"], d["ids"], swapped, d["w_scale"], T, topk, E, N, K)
     ok, err, bound = oracle.tolerance_ok(y_bad, y)
     assert not ok
+
+
+# --- stage-1 activation: silu(gate) * up ----------------------------------------
+
+def test_silu_mul_matches_library_sigmoid(oracle):
+    """silu(v) = v * sigmoid(v), with scipy's logistic sigmoid as the library
+    routine; gate is the first half of each row, up the second."""
+    from scipy.special import expit
+    rng = np.random.default_rng(9)
+    y = rng.normal(0.0, 30.0, (7, 64))
+    y[0, :4] = [0.0, -0.0, 750.0, -750.0]  # exact zero, saturated sigmoid both ways
+    out = oracle.silu_mul(y)
+    g, u = y[:, :32], y[:, 32:]
+    ref = g * expit(g) * u
+    assert np.allclose(out, ref, rtol=1e-14, atol=1e-300)
+    assert out[0, 0] == 0.0 and out[0, 2] == 750.0 * u[0, 2] and out[0, 3] == 0.0
+
+
+def test_silu_mul_odd_part_pins_the_gate_up_pairing(oracle):
+    """silu(g) - silu(-g) = g, so negating the gate half of W1 (flipping the
+    E2M1 sign bit of its codes) changes the activated output by exactly
+    gate_pre * up_pre; a swapped gate/up pairing fails this."""
+    T, E, topk, N, K = 10, 3, 2, 32, 128
+    d = wl.moe_inputs(T, E, topk, N, K, seed=12)
+    pre = oracle.mxfp4_moe_gemm(d["x"], d["ids"], d["w_fp4"], d["w_scale"], T, topk, E, N, K)
+    neg = d["w_fp4"].copy()
+    neg[:, : N // 2, :] ^= 0x88  # sign bit of both codes of every gate byte
+    pre_neg = oracle.mxfp4_moe_gemm(d["x"], d["ids"], neg, d["w_scale"], T, topk, E, N, K)
+    assert np.array_equal(pre_neg[..., : N // 2], -pre[..., : N // 2])
+    diff = oracle.silu_mul(pre) - oracle.silu_mul(pre_neg)
+    ref = pre[..., : N // 2] * pre[..., N // 2:]
+    assert np.allclose(diff, ref, rtol=1e-12, atol=1e-9)
+    # the same difference with the halves' roles swapped is 2 silu(up) gate
+    g, u = pre[..., : N // 2], pre[..., N // 2:]
+    swapped = u / (1.0 + np.exp(-u)) * g - u / (1.0 + np.exp(-u)) * (-g)
+    assert not np.allclose(swapped, ref, rtol=1e-3, atol=1e-3)

@@ -16,13 +16,14 @@ from __future__ import annotations
 import ctypes
 
 from . import _lib
-from ._lib import (BF16, DTYPE, F16, F32, INVALID_ARG, OK, PATH_AUTO, PATH_SKINNY, PATH_TILED,
-                   U4X8_I32, UNSUPPORTED, WobArgError, WobDtypeError, WobError)
+from ._lib import (ACT_NONE, ACT_SILU_MUL, BF16, DTYPE, F16, F32, INVALID_ARG, OK, PATH_AUTO,
+                   PATH_SKINNY, PATH_TILED, U4X8_I32, UNSUPPORTED, WobArgError, WobDtypeError,
+                   WobError)
 
 __all__ = [
     "gemm", "gemm_grouped", "mxfp4_moe_gemm", "moe_workspace_size", "w4a16_dequant",
     "mxfp4_dequant", "device_check", "WobError", "WobDtypeError", "WobArgError",
-    "PATH_AUTO", "PATH_SKINNY", "PATH_TILED",
+    "PATH_AUTO", "PATH_SKINNY", "PATH_TILED", "ACT_NONE", "ACT_SILU_MUL",
 ]
 
 
@@ -111,9 +112,10 @@ def moe_workspace_size(T: int, topk: int, E: int) -> int:
     return int(_lib.lib().mxfp4_moe_gemm_workspace_size(T, topk, E))
 
 
-def mxfp4_moe_gemm(x, topk_ids, w_fp4, w_scale, out=None, workspace=None):
-    """MoE stage 1: y[T,topk,N] bf16 from x [T,K] bf16, topk_ids [T,topk] int32,
-    w_fp4 [E,N,K/2] uint8 and w_scale [E,N,K/32] uint8 (E8M0)."""
+def mxfp4_moe_gemm(x, topk_ids, w_fp4, w_scale, out=None, workspace=None, act: int = ACT_NONE):
+    """MoE stage 1: x [T,K] bf16, topk_ids [T,topk] int32, w_fp4 [E,N,K/2] uint8 and
+    w_scale [E,N,K/32] uint8 (E8M0) -> y [T,topk,N] bf16 (act=ACT_NONE) or
+    y [T,topk,N/2] = silu(gate) * up (act=ACT_SILU_MUL)."""
     torch = _torch()
     T, K = x.shape
     topk = topk_ids.shape[1]
@@ -123,14 +125,15 @@ def mxfp4_moe_gemm(x, topk_ids, w_fp4, w_scale, out=None, workspace=None):
     if w_fp4.dtype != torch.uint8 or w_scale.dtype != torch.uint8:
         raise TypeError("w_fp4 and w_scale must be uint8")
     if out is None:
-        out = torch.empty((T, topk, N), dtype=torch.bfloat16, device=x.device)
+        nout = N // 2 if act == ACT_SILU_MUL else N
+        out = torch.empty((T, topk, nout), dtype=torch.bfloat16, device=x.device)
     need = moe_workspace_size(T, topk, E)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     dev = _check_device(x, topk_ids, w_fp4, w_scale, out, workspace)
     with torch.cuda.device(dev):
-        st = _lib.lib().mxfp4_moe_gemm(
-            _ptr(x), _ptr(topk_ids), _ptr(w_fp4), _ptr(w_scale), _ptr(out), T, topk, E, N, K,
+        st = _lib.lib().mxfp4_moe_gemm_act(
+            _ptr(x), _ptr(topk_ids), _ptr(w_fp4), _ptr(w_scale), _ptr(out), T, topk, E, N, K, act,
             _ptr(workspace), workspace.numel(), _stream(dev))
     _lib.check(st, "mxfp4_moe_gemm")
     return out

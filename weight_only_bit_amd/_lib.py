@@ -15,11 +15,12 @@ LIB_PATH = os.path.join(_PKG, "libweight_only_bit.so")
 OK, INVALID_ARG, DTYPE, UNSUPPORTED, HIP = 0, 1, 2, 3, 4
 F16, BF16, U4X8_I32, F32 = 0, 1, 2, 3
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
+ACT_NONE, ACT_SILU_MUL = 0, 1
 
 EXPORTS = [
     "wob_status_str", "wob_last_error", "wob_device_check",
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_grouped",
-    "mxfp4_moe_gemm_workspace_size", "mxfp4_moe_gemm",
+    "mxfp4_moe_gemm_workspace_size", "mxfp4_moe_gemm", "mxfp4_moe_gemm_act",
     "w4a16_dequant", "mxfp4_dequant",
 ]
 
@@ -38,6 +39,8 @@ _SIGNATURES = {
                                 _i64, _vp]),
     "mxfp4_moe_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
     "mxfp4_moe_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "mxfp4_moe_gemm_act": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i, _vp, _sz,
+                                _vp]),
     "w4a16_dequant": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _i64, _i64, _i64, _vp]),
     "mxfp4_dequant": (_i, [_vp, _vp, _vp, _i64, _i64, _vp]),
 }

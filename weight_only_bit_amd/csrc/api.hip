@@ -205,16 +205,22 @@ size_t mxfp4_moe_gemm_workspace_size(int64_t T, int64_t topk, int64_t E)
     return wob::moe_workspace_bytes(T, topk, E);
 }
 
-int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
-                   const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E, int64_t N,
-                   int64_t K, void *workspace, size_t workspace_bytes, void *stream)
+int mxfp4_moe_gemm_act(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
+                       const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E,
+                       int64_t N, int64_t K, int act, void *workspace, size_t workspace_bytes,
+                       void *stream)
 {
+    if (act != WOB_ACT_NONE && act != WOB_ACT_SILU_MUL)
+        return fail(WOB_INVALID_ARG, "unknown activation %d", act);
     if (T < 0 || topk < 1 || E < 1 || N < 0 || K < 32)
         return fail(WOB_INVALID_ARG, "bad shape T=%lld topk=%lld E=%lld N=%lld K=%lld",
                     (long long)T, (long long)topk, (long long)E, (long long)N, (long long)K);
     if (K % 64 != 0 || N % 16 != 0)
         return fail(WOB_INVALID_ARG, "need K %% 64 == 0 and N %% 16 == 0 (K=%lld N=%lld)",
                     (long long)K, (long long)N);
+    if (act == WOB_ACT_SILU_MUL && N % 32 != 0)
+        return fail(WOB_INVALID_ARG, "the silu(gate) * up activation needs N %% 32 == 0 (N=%lld)",
+                    (long long)N);
     // 32-bit in-kernel offsets: x rows (T*K*2 bytes), one expert's codes
     // (N*K/2 bytes) and the routed pair count T*topk.
     if (T > INT_MAX / 64 || topk > 64 || E > 4096 || N > INT_MAX / 2 || K > INT_MAX / 2 ||
@@ -236,9 +242,17 @@ int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
     if (s != WOB_OK)
         return s;
     return launched(wob::launch_mxfp4_moe(x, topk_ids, w_fp4, w_scale, y, (int)T, (int)topk,
-                                          (int)E, (int)N, (int)K, workspace,
+                                          (int)E, (int)N, (int)K, act, workspace,
                                           static_cast<hipStream_t>(stream)),
                     "mxfp4 moe");
+}
+
+int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
+                   const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E, int64_t N,
+                   int64_t K, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return mxfp4_moe_gemm_act(x, topk_ids, w_fp4, w_scale, y, T, topk, E, N, K, WOB_ACT_NONE,
+                              workspace, workspace_bytes, stream);
 }
 
 int w4a16_dequant(const int32_t *qweight, const void *scales, int scales_dtype,

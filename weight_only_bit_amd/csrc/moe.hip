@@ -152,7 +152,10 @@ struct GatherRows {
     __device__ __forceinline__ uint16_t *row(int r) const { return y + (size_t)pairs[r] * N; }
 };
 
-template <int MB>
+// The tile with MB 32-row blocks; ACT: the paired gate/up layout and the
+// fused silu(gate) * up store (I = N / 2 output columns), else the plain
+// pre-activation store.
+template <bool ACT, int MB>
 __device__ __forceinline__ void moe_run(const FmtFP4 &fmt, const int32_t *pairs, int rows, int topk,
                                         const uint16_t *x, uint16_t *y, int K, int N, int n0,
                                         uint8_t *smem, const TileLane &tl)
@@ -160,7 +163,7 @@ __device__ __forceinline__ void moe_run(const FmtFP4 &fmt, const int32_t *pairs,
     GatherRows<MB> g;
     g.pairs = pairs;
     g.y = y;
-    g.N = N;
+    g.N = ACT ? N / 2 : N;
 #pragma unroll
     for (int i = 0; i < 2 * MB; ++i) {
         const int p = pairs[min(16 * i + tl.rl, rows - 1)];
@@ -169,10 +172,13 @@ __device__ __forceinline__ void moe_run(const FmtFP4 &fmt, const int32_t *pairs,
     float16_t acc[2][MB];
     tile_mainloop<DT_BF16, MB>(fmt, g, reinterpret_cast<const uint8_t *>(x), K, n0, N, smem, tl,
                                acc);
-    tile_store<DT_BF16, MB>(acc, g, rows, n0, N, tl, smem);
+    if constexpr (ACT)
+        tile_store_silu_mul<DT_BF16, MB>(acc, g, rows, n0, N / 2, tl, smem);
+    else
+        tile_store<DT_BF16, MB>(acc, g, rows, n0, N, tl, smem);
 }
 
-template <int MB>
+template <bool ACT, int MB>
 __device__ __forceinline__ void moe_dispatch(int mb, const FmtFP4 &fmt, const int32_t *pairs,
                                              int rows, int topk, const uint16_t *x, uint16_t *y,
                                              int K, int N, int n0, uint8_t *smem,
@@ -180,11 +186,11 @@ __device__ __forceinline__ void moe_dispatch(int mb, const FmtFP4 &fmt, const in
 {
     if constexpr (MB > 1) {
         if (mb < MB) {
-            moe_dispatch<MB - 1>(mb, fmt, pairs, rows, topk, x, y, K, N, n0, smem, tl);
+            moe_dispatch<ACT, MB - 1>(mb, fmt, pairs, rows, topk, x, y, K, N, n0, smem, tl);
             return;
         }
     }
-    moe_run<MB>(fmt, pairs, rows, topk, x, y, K, N, n0, smem, tl);
+    moe_run<ACT, MB>(fmt, pairs, rows, topk, x, y, K, N, n0, smem, tl);
 }
 
 struct ZeroRows {
@@ -194,29 +200,35 @@ struct ZeroRows {
     __device__ __forceinline__ uint16_t *row(int r) const { return y + (size_t)pairs[r] * N; }
 };
 
+// One (expert tile, weight-row tile) pair per workgroup.  ACT: tiles of 128
+// output columns (128 gate rows + the matching 128 up rows), else 256.
+template <bool ACT>
 __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w_fp4,
     const uint8_t *__restrict__ w_scale, uint16_t *__restrict__ y, const int32_t *__restrict__ hdr,
     const int4 *__restrict__ tiles, const int32_t *__restrict__ sorted, int topk, int E, int N,
     int K, int n_nt)
 {
+    constexpr int TW = ACT ? TL_TN / 2 : TL_TN; // output columns per tile
     extern __shared__ __align__(16) uint8_t smem[];
     const int t = xcd_tile(hdr[0] * n_nt);
     if (t < 0)
         return;
     const int i = t / n_nt;
-    const int n0 = (t - i * n_nt) * TL_TN;
+    const int n0 = (t - i * n_nt) * TW;
     const int4 te = tiles[i];
     const int e = te.x, rows = te.z;
     const int32_t *pairs = sorted + te.y;
+    const int Nout = ACT ? N / 2 : N;
     if (e >= E) {
-        tile_store_zero(ZeroRows{pairs, y, N}, rows, n0, N);
+        tile_store_zero<TW>(ZeroRows{pairs, y, Nout}, rows, n0, Nout);
         return;
     }
     const TileLane tl;
     const FmtFP4 fmt(w_fp4 + (size_t)e * N * (K >> 1), w_scale + (size_t)e * N * (K >> 5), N, K,
-                     n0, tl);
-    moe_dispatch<TL_MB_MAX>((rows + 31) >> 5, fmt, pairs, rows, topk, x, y, K, N, n0, smem, tl);
+                     n0, tl, ACT ? N / 2 : 0);
+    moe_dispatch<ACT, TL_MB_MAX>((rows + 31) >> 5, fmt, pairs, rows, topk, x, y, K, N, n0, smem,
+                                 tl);
 }
 
 } // namespace
@@ -229,7 +241,7 @@ size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t E)
 
 hipError_t launch_mxfp4_moe(const void *x, const int32_t *ids, const uint8_t *w_fp4,
                             const uint8_t *w_scale, void *y, int T, int topk, int E, int N, int K,
-                            void *workspace, hipStream_t stream)
+                            int act, void *workspace, hipStream_t stream)
 {
     const int64_t P = (int64_t)T * topk;
     const MoeWs w = carve(workspace, P, E);
@@ -239,18 +251,22 @@ hipError_t launch_mxfp4_moe(const void *x, const int32_t *ids, const uint8_t *w_
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    static hipError_t attr = hipErrorNotReady;
-    if (attr != hipSuccess)
-        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(moe_gemm_kernel),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   tile_lds_bytes(TL_MB_MAX));
-    if (attr != hipSuccess)
-        return attr;
-    const int n_nt = (N + TL_TN - 1) / TL_TN;
+    auto kern = act ? moe_gemm_kernel<true> : moe_gemm_kernel<false>;
+    static hipError_t attr[2] = {hipErrorNotReady, hipErrorNotReady};
+    hipError_t &ae = attr[act ? 1 : 0];
+    if (ae != hipSuccess)
+        ae = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 tile_lds_bytes(TL_MB_MAX));
+    if (ae != hipSuccess)
+        return ae;
+    const int tw = act ? TL_TN / 2 : TL_TN;
+    const int nout = act ? N / 2 : N;
+    const int n_nt = (nout + tw - 1) / tw;
     const int64_t grid = 8 * (((int64_t)max_tiles(P, E) * n_nt + 7) / 8);
     if (grid > INT32_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(moe_gemm_kernel, dim3((unsigned)grid), dim3(TL_THREADS),
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(TL_THREADS),
                        (size_t)tile_lds_bytes(TL_MB_MAX), stream,
                        static_cast<const uint16_t *>(x), w_fp4, w_scale, static_cast<uint16_t *>(y),
                        w.hdr, w.tiles, w.sorted, topk, E, N, K, n_nt);

@@ -32,7 +32,7 @@ hipError_t launch_w4a16_grouped(const W4Args &a, const int64_t *m_offsets, int n
 size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t E);
 hipError_t launch_mxfp4_moe(const void *x, const int32_t *ids, const uint8_t *w_fp4,
                             const uint8_t *w_scale, void *y, int T, int topk, int E, int N, int K,
-                            void *workspace, hipStream_t stream);
+                            int act, void *workspace, hipStream_t stream);
 
 // Dequantization probes.
 hipError_t launch_w4a16_dequant(const uint32_t *qweight, const void *scales, const uint32_t *qzeros,

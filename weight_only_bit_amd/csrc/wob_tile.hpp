@@ -53,6 +53,7 @@
 // Weight formats (4-bit codes, K/2 bytes per row, at `wq`) plug in as a
 // policy with:
 //    const uint8_t *wq;                   codes of row 0 of the matrix
+//    int tile_row(int n0, int N, int t) const;  matrix row of tile row t (clamped)
 //    struct Meta;                         a lane's scales / zero-points of a span
 //    static constexpr int NLOADS;         vector-memory operations per load_meta()
 //    void load_meta(int span, Meta &m) const;
@@ -178,7 +179,7 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
     uint32_t crow[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
-        crow[jj] = (uint32_t)min(n0 + 16 * (4 * tl.wave + jj) + (tl.lane >> 2), N - 1) * rowb;
+        crow[jj] = (uint32_t)fmt.tile_row(n0, N, 16 * (4 * tl.wave + jj) + (tl.lane >> 2)) * rowb;
     const uint32_t cpiece = 16u * (uint32_t)((tl.lane & 3) ^ (tl.lane >> 4));
     auto issue_w = [&](int span, int buf) __attribute__((always_inline)) {
         const uint32_t kb = min((uint32_t)span * 64u + cpiece, rowb - 16u);
@@ -351,14 +352,55 @@ __device__ __forceinline__ void tile_store(const float16_t (&acc)[2][MB], const 
     }
 }
 
-// Zero rows [0, rows) of a tile's 256-column range (expert rows whose id is
+// Store with the fused stage-1 activation (paired layout, see FmtFP4): the
+// same accumulator register of blocks nb = 0 and 1 holds gate and up of one
+// output column, n = n0 + 32 w + 8 g4 + 4 h + j, so out = silu(gate) * up in
+// fp32 with silu(v) = v / (1 + e^-v), rounded once to the activation dtype.
+// Staged through LDS as for tile_store: 128 output columns per tile row.
+template <int DT, int MB, class YRows>
+__device__ __forceinline__ void tile_store_silu_mul(const float16_t (&acc)[2][MB], const YRows &yr,
+                                                   int rows, int n0, int I, const TileLane &tl,
+                                                   uint8_t *smem)
+{
+    constexpr int TM = 32 * MB;
+    constexpr int RS = TL_TN + 16; // LDS bytes per staged row (128 values + pad)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int m = 32 * mb + tl.nl;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int c = 32 * tl.wave + 8 * g4 + 4 * tl.h;
+            float o4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float g = acc[0][mb][4 * g4 + j];
+                const float u = acc[1][mb][4 * g4 + j];
+                o4[j] = g / (1.0f + expf(-g)) * u;
+            }
+            uint2 o;
+            o.x = f32x2_to_act2<DT>(o4[0], o4[1]);
+            o.y = f32x2_to_act2<DT>(o4[2], o4[3]);
+            *reinterpret_cast<uint2 *>(smem + m * RS + 2 * c) = o;
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < TM * 16; i += TL_THREADS) {
+        const int r = i >> 4, c = i & 15;
+        const int n = n0 + 8 * c;
+        if (r < rows && n < I)
+            *reinterpret_cast<u32x4 *>(yr.row(r) + n) =
+                *reinterpret_cast<const u32x4 *>(smem + r * RS + 16 * c);
+    }
+}
+
+// Zero rows [0, rows) of a tile's WIDTH-column range (expert rows whose id is
 // out of range).
-template <class YRows>
+template <int WIDTH, class YRows>
 __device__ __forceinline__ void tile_store_zero(const YRows &yr, int rows, int n0, int N)
 {
-    for (int i = threadIdx.x; i < rows * (TL_TN / 4); i += TL_THREADS) {
-        const int r = i / (TL_TN / 4);
-        const int n = n0 + 4 * (i % (TL_TN / 4));
+    for (int i = threadIdx.x; i < rows * (WIDTH / 4); i += TL_THREADS) {
+        const int r = i / (WIDTH / 4);
+        const int n = n0 + 4 * (i % (WIDTH / 4));
         if (n < N)
             *reinterpret_cast<uint2 *>(yr.row(r) + n) = uint2{0u, 0u};
     }
@@ -412,6 +454,8 @@ struct FmtW4 {
         }
     }
 
+    __device__ __forceinline__ int tile_row(int n0, int N, int t) const { return min(n0 + t, N - 1); }
+
     __device__ __forceinline__ void load_meta(int span, Meta &m) const
     {
 #pragma unroll
@@ -439,6 +483,12 @@ struct FmtW4 {
 // MXFP4: E2M1 codes w_fp4[N][K/2] (even k in the low nibble), E8M0 scales
 // w_scale[N][K/32]; needs K % 64 == 0 so a lane's two 32-wide slices share
 // one aligned 16-bit scale load.
+//
+// Paired layout (half = N / 2 > 0, for the fused gate/up activation): the
+// tile's weight rows come in pairs, gate row j and up row half + j, so that
+// block nb = 0 of wave w holds gate rows n0 + 32 w .. +31 and block nb = 1
+// the matching up rows; tile row t = 64 w + 32 nb + i maps to matrix row
+// nb * half + n0 + 32 w + i.
 struct FmtFP4 {
     static constexpr int NLOADS = 2;
     struct Meta {
@@ -446,20 +496,29 @@ struct FmtFP4 {
     };
     const uint8_t *wq, *ws;
     uint32_t soff[2];
-    int K, h;
+    int K, h, half;
 
     __device__ FmtFP4(const uint8_t *w_fp4, const uint8_t *w_scale, int N, int K_, int n0,
-                      const TileLane &tl)
+                      const TileLane &tl, int half_ = 0)
     {
         wq = w_fp4;
         ws = w_scale;
         K = K_;
         h = tl.h;
+        half = half_;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-            const int n = min(n0 + 64 * tl.wave + 32 * nb + tl.nl, N - 1);
+            const int n = tile_row(n0, N, 64 * tl.wave + 32 * nb + tl.nl);
             soff[nb] = (uint32_t)n * (uint32_t)(K >> 5);
         }
+    }
+
+    __device__ __forceinline__ int tile_row(int n0, int N, int t) const
+    {
+        if (!half)
+            return min(n0 + t, N - 1);
+        const int nb = (t >> 5) & 1;
+        return nb * half + min(n0 + 32 * (t >> 6) + (t & 31), half - 1);
     }
 
     __device__ __forceinline__ void load_meta(int span, Meta &m) const
