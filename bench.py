@@ -43,10 +43,14 @@ MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA, published
 MALL_BYTES = 256 << 20         # Infinity Cache
 FETCH_FACTOR_DEFAULT = 2.0     # FETCH_SIZE reads half of a device copy's bytes on this part
 
+# Sources of the kernel each workload's roofline entry describes: a committed
+# counter summary counts only while these are unchanged.
 KERNEL_SOURCES = {
-    "w4a16": ["weight_only_bit_amd/csrc/skinny.hip", "weight_only_bit_amd/csrc/tiled.hip",
+    "skinny": ["weight_only_bit_amd/csrc/skinny.hip", "weight_only_bit_amd/csrc/wob_device.hpp"],
+    "tiled": ["weight_only_bit_amd/csrc/tiled.hip", "weight_only_bit_amd/csrc/wob_tile.hpp",
               "weight_only_bit_amd/csrc/wob_device.hpp"],
-    "moe": ["weight_only_bit_amd/csrc/moe.hip", "weight_only_bit_amd/csrc/wob_device.hpp"],
+    "moe": ["weight_only_bit_amd/csrc/moe.hip", "weight_only_bit_amd/csrc/wob_tile.hpp",
+            "weight_only_bit_amd/csrc/wob_device.hpp"],
 }
 
 
@@ -59,8 +63,10 @@ def source_sha(kind: str) -> str:
 
 
 def committed_traffic(key: str, kind: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if the
-    kernel sources are unchanged since the counters were taken; else None."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE in KiB per dispatch of the
+    dominant kernel, and the FETCH_SIZE scale measured on a plain device copy),
+    if the kernel sources are unchanged since the counters were taken; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -153,19 +159,19 @@ def bench_w4a16(wkey: str, steps: int, warmup: int):
         achieved = nbytes / (kern_ms * 1e-3) / 1e9
         res["roofline"] = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
                                unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                               traffic=committed_traffic(wkey, "w4a16"))
+                               traffic=committed_traffic(wkey, "skinny"))
     else:
         res["tflops"] = round(flops / (graph_ms * 1e-3) / 1e12, 2)
         achieved = flops / (kern_ms * 1e-3) / 1e12
         res["roofline"] = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_PEAK_TFLOPS,
                                unit="TFLOP/s", frac=round(achieved / MFMA_PEAK_TFLOPS, 4),
-                               traffic=committed_traffic(wkey, "w4a16"))
+                               traffic=committed_traffic(wkey, "tiled"))
     del bufs, ys
     torch.cuda.empty_cache()
     return res, d
 
 
-def bench_moe(wkey: str, steps: int, warmup: int):
+def bench_moe(wkey: str, steps: int, warmup: int, act: int = 0):
     import weight_only_bit_amd as wob
     torch = _torch()
     w = wl.BY_KEY[wkey]
@@ -182,22 +188,25 @@ def bench_moe(wkey: str, steps: int, warmup: int):
     for _ in range(copies):
         bufs.append(dict(x=dev(d["x"].view(np.int16)).view(torch.bfloat16), ids=dev(d["ids"]),
                          w=dev(d["w_fp4"]), s=dev(d["w_scale"])))
-    ys = [torch.empty((T, topk, N), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+    nout = N // 2 if act else N
+    ys = [torch.empty((T, topk, nout), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
     ws = torch.empty(max(wob.moe_workspace_size(T, topk, E), 16), dtype=torch.uint8, device="cuda")
 
     def step(i):
         b = bufs[i % copies]
-        wob.mxfp4_moe_gemm(b["x"], b["ids"], b["w"], b["s"], out=ys[i % copies], workspace=ws)
+        wob.mxfp4_moe_gemm(b["x"], b["ids"], b["w"], b["s"], out=ys[i % copies], workspace=ws,
+                           act=act)
 
     graph_ms = kern_ms = _time_steps(step, steps, warmup)
-    res = dict(workload=w.desc, T=T, E=E, topk=topk, N=N, K=K, dtype="bf16 x mxfp4",
+    res = dict(workload=w.desc + (" + fused silu(gate)*up" if act else ""), T=T, E=E, topk=topk,
+               N=N, K=K, dtype="bf16 x mxfp4",
                copies=copies, bytes_per_call=nbytes, flops_per_call=flops,
                us_per_call=round(graph_ms * 1e3, 3),
                tflops=round(flops / (graph_ms * 1e-3) / 1e12, 2))
     achieved = flops / (kern_ms * 1e-3) / 1e12
     res["roofline"] = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_PEAK_TFLOPS,
                            unit="TFLOP/s", frac=round(achieved / MFMA_PEAK_TFLOPS, 4),
-                           traffic=committed_traffic(wkey, "moe"))
+                           traffic=committed_traffic(wkey + ("_silu" if act else ""), "moe"))
     del bufs, ys
     torch.cuda.empty_cache()
     return res, d
@@ -223,7 +232,7 @@ def cpu_baseline_decode(d, budget_s: float = 10.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_gemv", choices=[w.key for w in wl.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -289,6 +298,10 @@ def main():
                 others[w.key] = r
             except Exception as e:  # report, do not hide: the entry says what failed
                 others[w.key] = dict(workload=w.desc, error=f"{type(e).__name__}: {e}")
+        try:
+            others["moe_stage1_silu"], _ = bench_moe("moe_stage1", args.steps, args.warmup, act=1)
+        except Exception as e:
+            others["moe_stage1_silu"] = dict(workload="moe_stage1 + silu", error=f"{type(e).__name__}: {e}")
         line["others"] = others
     print(json.dumps(line), flush=True)
 
