@@ -156,7 +156,7 @@ struct GatherRows {
 // fused silu(gate) * up store (I = N / 2 output columns), else the plain
 // pre-activation store.
 template <bool ACT, int MB>
-__device__ __forceinline__ void moe_run(const FmtFP4 &fmt, const int32_t *pairs, int rows, int topk,
+__device__ __forceinline__ void moe_run(const FmtFP4<ACT> &fmt, const int32_t *pairs, int rows, int topk,
                                         const uint16_t *x, uint16_t *y, int K, int N, int n0,
                                         uint8_t *smem, const TileLane &tl)
 {
@@ -179,7 +179,7 @@ __device__ __forceinline__ void moe_run(const FmtFP4 &fmt, const int32_t *pairs,
 }
 
 template <bool ACT, int MB>
-__device__ __forceinline__ void moe_dispatch(int mb, const FmtFP4 &fmt, const int32_t *pairs,
+__device__ __forceinline__ void moe_dispatch(int mb, const FmtFP4<ACT> &fmt, const int32_t *pairs,
                                              int rows, int topk, const uint16_t *x, uint16_t *y,
                                              int K, int N, int n0, uint8_t *smem,
                                              const TileLane &tl)
@@ -225,8 +225,8 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
         return;
     }
     const TileLane tl;
-    const FmtFP4 fmt(w_fp4 + (size_t)e * N * (K >> 1), w_scale + (size_t)e * N * (K >> 5), N, K,
-                     n0, tl, ACT ? N / 2 : 0);
+    const FmtFP4<ACT> fmt(w_fp4 + (size_t)e * N * (K >> 1), w_scale + (size_t)e * N * (K >> 5), N,
+                          K, n0, tl);
     moe_dispatch<ACT, TL_MB_MAX>((rows + 31) >> 5, fmt, pairs, rows, topk, x, y, K, N, n0, smem,
                                  tl);
 }

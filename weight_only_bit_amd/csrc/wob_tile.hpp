@@ -57,6 +57,8 @@
 //    struct Meta;                         a lane's scales / zero-points of a span
 //    static constexpr int NLOADS;         vector-memory operations per load_meta()
 //    void load_meta(int span, Meta &m) const;
+//    static constexpr bool ZERO_BY_SCALE;  slices past K zeroed through their scales
+//    void zero_past_k(int span, Meta &m) const;  scales of slices past K -> 0
 //    u32x4 dequant(uint32_t word, const Meta &m, int nb, int st) const;
 #pragma once
 
@@ -248,12 +250,22 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
             const int p = (8 * tl.h + st) ^ (R & 15);
             return *reinterpret_cast<const u32x4 *>(xb + R * TL_ROWB + 16 * p);
         };
+        // Only a span that crosses K (uniform test) has slices past K.  Their
+        // weights become zero: through zero scales (one select per slice), or
+        // per operand word (one select per word), whichever the format's
+        // kernel measured faster (the choice changes the compiler's register
+        // allocation of the whole loop).
         const bool ktail = span * TL_SPAN + TL_SPAN > K;
+        if constexpr (Fmt::ZERO_BY_SCALE) {
+            if (ktail)
+                fmt.zero_past_k(span, cur);
+        }
         auto dq = [&](int nb, int st) __attribute__((always_inline)) {
             u32x4 v = fmt.dequant(cw[nb][st >> 2][st & 3], cur, nb, st);
-            // only a span that crosses K (uniform test) zeroes the slices past K
-            if (ktail && span * TL_SPAN + 64 * tl.h + 32 * (st >> 2) >= K)
-                v = u32x4{0, 0, 0, 0};
+            if constexpr (!Fmt::ZERO_BY_SCALE) {
+                if (ktail && span * TL_SPAN + 64 * tl.h + 32 * (st >> 2) >= K)
+                    v = u32x4{0, 0, 0, 0};
+            }
             return v;
         };
         u32x4 wc[2], wn[2], xc[MB], xn[MB];
@@ -428,6 +440,7 @@ __device__ __forceinline__ int xcd_tile(int tiles)
 template <int DT, bool HAS_Z>
 struct FmtW4 {
     static constexpr int NLOADS = HAS_Z ? 8 : 4;
+    static constexpr bool ZERO_BY_SCALE = true;
     struct Meta {
         uint32_t s[2][2], z[2][2];
     };
@@ -461,7 +474,7 @@ struct FmtW4 {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int k = span * TL_SPAN + 64 * h + 32 * hf;
-            const int kc = min(k, K - 32); // slice past K: clamped load, zeroed at dequant
+            const int kc = min(k, K - 32); // slice past K: clamped load, scale zeroed at use
             const uint32_t grp = (uint32_t)(kc >> (5 + gshift));
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
@@ -470,6 +483,16 @@ struct FmtW4 {
                                     : 0x88888888u;
             }
         }
+    }
+
+    __device__ __forceinline__ void zero_past_k(int span, Meta &m) const
+    {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+            if (span * TL_SPAN + 64 * h + 32 * hf >= K)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    m.s[nb][hf] = 0u; // (q - z) * 0 is a zero of either sign
     }
 
     __device__ __forceinline__ u32x4 dequant(uint32_t word, const Meta &m, int nb, int st) const
@@ -484,28 +507,29 @@ struct FmtW4 {
 // w_scale[N][K/32]; needs K % 64 == 0 so a lane's two 32-wide slices share
 // one aligned 16-bit scale load.
 //
-// Paired layout (half = N / 2 > 0, for the fused gate/up activation): the
-// tile's weight rows come in pairs, gate row j and up row half + j, so that
+// Paired layout (PAIRED, for the fused gate/up activation): the tile's
+// weight rows come in pairs, gate row j and up row N/2 + j, so that
 // block nb = 0 of wave w holds gate rows n0 + 32 w .. +31 and block nb = 1
 // the matching up rows; tile row t = 64 w + 32 nb + i maps to matrix row
-// nb * half + n0 + 32 w + i.
+// nb * N/2 + n0 + 32 w + i.
+template <bool PAIRED>
 struct FmtFP4 {
     static constexpr int NLOADS = 2;
+    static constexpr bool ZERO_BY_SCALE = false;
     struct Meta {
         uint32_t s[2]; // E8M0 bytes of slices hf = 0 (low byte) and 1
     };
     const uint8_t *wq, *ws;
     uint32_t soff[2];
-    int K, h, half;
+    int K, h;
 
     __device__ FmtFP4(const uint8_t *w_fp4, const uint8_t *w_scale, int N, int K_, int n0,
-                      const TileLane &tl, int half_ = 0)
+                      const TileLane &tl)
     {
         wq = w_fp4;
         ws = w_scale;
         K = K_;
         h = tl.h;
-        half = half_;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             const int n = tile_row(n0, N, 64 * tl.wave + 32 * nb + tl.nl);
@@ -513,12 +537,16 @@ struct FmtFP4 {
         }
     }
 
+    // Matrix row of tile row t; PAIRED: t = 64 w + 32 nb + i is row
+    // nb * N/2 + n0 + 32 w + i (gate rows, then the matching up rows).
     __device__ __forceinline__ int tile_row(int n0, int N, int t) const
     {
-        if (!half)
+        if constexpr (!PAIRED) {
             return min(n0 + t, N - 1);
-        const int nb = (t >> 5) & 1;
-        return nb * half + min(n0 + 32 * (t >> 6) + (t & 31), half - 1);
+        } else {
+            const int half = N >> 1;
+            return ((t >> 5) & 1) * half + min(n0 + 32 * (t >> 6) + (t & 31), half - 1);
+        }
     }
 
     __device__ __forceinline__ void load_meta(int span, Meta &m) const
@@ -528,6 +556,16 @@ struct FmtFP4 {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
             m.s[nb] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + kg);
+    }
+
+    __device__ __forceinline__ void zero_past_k(int span, Meta &m) const
+    {
+        // K % 64 == 0: both 32-wide slices of a lane are inside K or past it;
+        // E8M0 byte 0 becomes the scale 0.0 (see e8m0_to_f32)
+        if (span * TL_SPAN + 64 * h >= K)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                m.s[nb] = 0u;
     }
 
     __device__ __forceinline__ u32x4 dequant(uint32_t word, const Meta &m, int nb, int st) const
