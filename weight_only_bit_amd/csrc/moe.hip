@@ -6,32 +6,35 @@
 //
 // Two kernels on the caller's stream:
 //  1. Routing (one workgroup): histogram of the expert ids in LDS, prefix sums
-//     of the rows and of the 256-row tiles per expert, a tile table
+//     of the rows and of the 128-row tiles per expert, a tile table
 //     {expert, first sorted row, rows} and the pairs sorted by expert (order
 //     inside an expert is arbitrary; every output row is computed the same
 //     way wherever it sits in a tile).  Ids outside [0, E) form one extra
 //     "expert" whose tiles write zero rows.
 //  2. Grouped MFMA GEMM: the cooperative-tile pipeline of wob_tile.hpp with the
-//     MXFP4 weight format.  A workgroup takes one (expert tile, 256 weight
+//     MXFP4 weight format.  A workgroup takes one (expert tile, 512 weight
 //     rows) pair; its activation rows are gathered from x by token, the FP4
 //     words are expanded to bfloat16 with v_cvt_scalef32_pk_bf16_fp4 (one
 //     conversion per byte, two elements each, the E8M0 byte placed in the
 //     binary32 exponent as the scale), v_mfma_f32_32x32x16_bf16 multiplies,
 //     and the epilogue scatters rows to their pair index.  Stores are guarded
 //     by the tile's row count and by N, so a tile that overhangs the weight
-//     rows (N not a multiple of 256) never writes into neighbouring cells: the
+//     rows (N not a multiple of 512) never writes into neighbouring cells: the
 //     failure the page's store guard fixes.
 //
-// An expert's rows form one tile when there are at most 256 of them, so its
-// weights are dequantized once; the tile multiplies only the 32-row blocks
-// its row count needs.
+// An expert's rows form one tile when there are at most 128 of them (the
+// average expert of a 1024-token, 32-expert, top-4 batch), so its weights are
+// dequantized once; the tile multiplies only the 32-row blocks its row count
+// needs.
 #include "wob_internal.hpp"
 #include "wob_tile.hpp"
 
 namespace wob {
 namespace {
 
-constexpr int MOE_TM = 32 * TL_MB_MAX; // rows per expert tile
+constexpr int MOE_NB = 2;                           // weight blocks per wave
+constexpr int MOE_TM = TileGeo<MOE_NB>::TM_MAX;     // rows per expert tile
+constexpr int MOE_TN = TileGeo<MOE_NB>::TN;         // weight rows per tile
 constexpr int ROUTE_THREADS = 1024;
 
 struct MoeWs {
@@ -156,9 +159,9 @@ struct GatherRows {
 // fused silu(gate) * up store (I = N / 2 output columns), else the plain
 // pre-activation store.
 template <bool ACT, int MB>
-__device__ __forceinline__ void moe_run(const FmtFP4<ACT> &fmt, const int32_t *pairs, int rows, int topk,
-                                        const uint16_t *x, uint16_t *y, int K, int N, int n0,
-                                        uint8_t *smem, const TileLane &tl)
+__device__ __forceinline__ void moe_run(const FmtFP4<ACT, MOE_NB> &fmt, const int32_t *pairs,
+                                        int rows, int topk, const uint16_t *x, uint16_t *y, int K,
+                                        int N, int n0, uint8_t *smem, const TileLane &tl)
 {
     GatherRows<MB> g;
     g.pairs = pairs;
@@ -169,20 +172,20 @@ __device__ __forceinline__ void moe_run(const FmtFP4<ACT> &fmt, const int32_t *p
         const int p = pairs[min(16 * i + tl.rl, rows - 1)];
         g.xo[i] = (uint32_t)(p / topk) * (uint32_t)K * 2u;
     }
-    float16_t acc[2][MB];
-    tile_mainloop<DT_BF16, MB>(fmt, g, reinterpret_cast<const uint8_t *>(x), K, n0, N, smem, tl,
-                               acc);
+    float16_t acc[MOE_NB][MB];
+    tile_mainloop<DT_BF16, MOE_NB, MB>(fmt, g, reinterpret_cast<const uint8_t *>(x), K, n0, N,
+                                       smem, tl, acc);
     if constexpr (ACT)
-        tile_store_silu_mul<DT_BF16, MB>(acc, g, rows, n0, N / 2, tl, smem);
+        tile_store_silu_mul<DT_BF16, MOE_NB, MB>(acc, g, rows, n0, N / 2, tl, smem);
     else
-        tile_store<DT_BF16, MB>(acc, g, rows, n0, N, tl, smem);
+        tile_store<DT_BF16, MOE_NB, MB>(acc, g, rows, n0, N, tl, smem);
 }
 
 template <bool ACT, int MB>
-__device__ __forceinline__ void moe_dispatch(int mb, const FmtFP4<ACT> &fmt, const int32_t *pairs,
-                                             int rows, int topk, const uint16_t *x, uint16_t *y,
-                                             int K, int N, int n0, uint8_t *smem,
-                                             const TileLane &tl)
+__device__ __forceinline__ void moe_dispatch(int mb, const FmtFP4<ACT, MOE_NB> &fmt,
+                                             const int32_t *pairs, int rows, int topk,
+                                             const uint16_t *x, uint16_t *y, int K, int N, int n0,
+                                             uint8_t *smem, const TileLane &tl)
 {
     if constexpr (MB > 1) {
         if (mb < MB) {
@@ -200,8 +203,8 @@ struct ZeroRows {
     __device__ __forceinline__ uint16_t *row(int r) const { return y + (size_t)pairs[r] * N; }
 };
 
-// One (expert tile, weight-row tile) pair per workgroup.  ACT: tiles of 128
-// output columns (128 gate rows + the matching 128 up rows), else 256.
+// One (expert tile, weight-row tile) pair per workgroup.  ACT: tiles of 256
+// output columns (256 gate rows + the matching 256 up rows), else 512.
 template <bool ACT>
 __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w_fp4,
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
     const int4 *__restrict__ tiles, const int32_t *__restrict__ sorted, int topk, int E, int N,
     int K, int n_nt)
 {
-    constexpr int TW = ACT ? TL_TN / 2 : TL_TN; // output columns per tile
+    constexpr int TW = ACT ? MOE_TN / 2 : MOE_TN; // output columns per tile
     extern __shared__ __align__(16) uint8_t smem[];
     const int t = xcd_tile(hdr[0] * n_nt);
     if (t < 0)
@@ -225,10 +228,10 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
         return;
     }
     const TileLane tl;
-    const FmtFP4<ACT> fmt(w_fp4 + (size_t)e * N * (K >> 1), w_scale + (size_t)e * N * (K >> 5), N,
-                          K, n0, tl);
-    moe_dispatch<ACT, TL_MB_MAX>((rows + 31) >> 5, fmt, pairs, rows, topk, x, y, K, N, n0, smem,
-                                 tl);
+    const FmtFP4<ACT, MOE_NB> fmt(w_fp4 + (size_t)e * N * (K >> 1),
+                                  w_scale + (size_t)e * N * (K >> 5), N, K, n0, tl);
+    moe_dispatch<ACT, TileGeo<MOE_NB>::MB_MAX>((rows + 31) >> 5, fmt, pairs, rows, topk, x, y, K,
+                                               N, n0, smem, tl);
 }
 
 } // namespace
@@ -257,17 +260,17 @@ hipError_t launch_mxfp4_moe(const void *x, const int32_t *ids, const uint8_t *w_
     if (ae != hipSuccess)
         ae = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 tile_lds_bytes(TL_MB_MAX));
+                                 TileGeo<MOE_NB>::lds_bytes(TileGeo<MOE_NB>::MB_MAX));
     if (ae != hipSuccess)
         return ae;
-    const int tw = act ? TL_TN / 2 : TL_TN;
+    const int tw = act ? MOE_TN / 2 : MOE_TN;
     const int nout = act ? N / 2 : N;
     const int n_nt = (nout + tw - 1) / tw;
     const int64_t grid = 8 * (((int64_t)max_tiles(P, E) * n_nt + 7) / 8);
     if (grid > INT32_MAX)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(TL_THREADS),
-                       (size_t)tile_lds_bytes(TL_MB_MAX), stream,
+                       (size_t)TileGeo<MOE_NB>::lds_bytes(TileGeo<MOE_NB>::MB_MAX), stream,
                        static_cast<const uint16_t *>(x), w_fp4, w_scale, static_cast<uint16_t *>(y),
                        w.hdr, w.tiles, w.sorted, topk, E, N, K, n_nt);
     return hipGetLastError();

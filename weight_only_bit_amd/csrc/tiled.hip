@@ -1,18 +1,19 @@
 // Cooperative-tile MFMA W4A16 GEMM on gfx950 (prefill, M >= 9; any M works)
 // and its ragged grouped form.
 //
-// One workgroup computes a 256 x TM output tile (weight rows x activation
-// rows) with the shared pipeline of wob_tile.hpp: the 256 weight rows are
+// One workgroup computes a TN x TM output tile (weight rows x activation
+// rows) with the shared pipeline of wob_tile.hpp: the TN weight rows are
 // dequantized once per tile, the activation rows stream through LDS, and
-// v_mfma_f32_32x32x16_{f16,bf16} does the products.  A tile holds up to 256
-// activation rows (eight 32-row blocks); the number of blocks actually
+// v_mfma_f32_32x32x16_{f16,bf16} does the products.  Tiles are 512 weight
+// rows by up to 128 activation rows (TILED_NB = 4 weight blocks per wave,
+// four 32-row activation blocks); the number of activation blocks actually
 // multiplied follows the tile's row count, so a short last tile (or a short
 // group) costs only the blocks it needs.
 //
-// Dense form: tiles cover rows [32 * MBMAX * mt, ...) of x and y.
+// Dense form: tiles cover rows [TM_MAX * mt, ...) of x and y.
 // Grouped form ("contiguous grouped" GEMM): group e owns rows
 // [m_offsets[e], m_offsets[e+1]) of x and y and its own packed weights; each
-// group is cut into tiles of 256 rows.  The group table stays on the device:
+// group is cut into tiles of TM_MAX rows.  The group table stays on the device:
 // every workgroup derives its (group, tile) from the offsets with wave-wide
 // prefix sums, so no host synchronization or workspace is needed.
 #include "wob_internal.hpp"
@@ -23,16 +24,19 @@
 namespace wob {
 namespace {
 
+constexpr int TILED_NB = 2; // 32-row weight blocks per wave: 256 x 256 tiles
+
 // Contiguous activation rows m0 .. m0 + rows - 1 of x[.][K] and y[.][N].
+// Byte offset of row min(16 i + rl, rows - 1): rowb (16 i + rl) clamped to
+// rowb (rows - 1), one add and one min per copy.
 struct ContigRows {
-    int rl, rows;
-    uint32_t rowb; // bytes per activation row
+    int rows;
+    uint32_t o0;   // rowb * rl (this lane's first row)
+    uint32_t s16;  // rowb * 16
+    uint32_t omax; // rowb * (rows - 1)
     uint16_t *y0;  // output row m0
     int N;
-    __device__ __forceinline__ uint32_t off(int i) const
-    {
-        return rowb * (uint32_t)min(16 * i + rl, rows - 1);
-    }
+    __device__ __forceinline__ uint32_t off(int i) const { return min(o0 + (uint32_t)i * s16, omax); }
     __device__ __forceinline__ uint16_t *row(int r) const { return y0 + (size_t)r * N; }
 };
 
@@ -113,39 +117,40 @@ __device__ bool grouped_tile(const int64_t *off, int G, int total_M, int TM, int
     return false;
 }
 
-template <int DT, int MB, class Fmt>
+template <int DT, int NB, int MB, class Fmt>
 __device__ __forceinline__ void run_tile(const Fmt &fmt, const ContigRows &rws, const uint8_t *xbase,
                                          int K, int N, int n0, uint8_t *smem, const TileLane &tl)
 {
-    float16_t acc[2][MB];
-    tile_mainloop<DT, MB>(fmt, rws, xbase, K, n0, N, smem, tl, acc);
-    tile_store<DT, MB>(acc, rws, rws.rows, n0, N, tl, smem);
+    float16_t acc[NB][MB];
+    tile_mainloop<DT, NB, MB>(fmt, rws, xbase, K, n0, N, smem, tl, acc);
+    tile_store<DT, NB, MB>(acc, rws, rws.rows, n0, N, tl, smem);
 }
 
 // Runs the tile with the smallest block count that covers `rows`.
-template <int DT, int MB, class Fmt>
+template <int DT, int NB, int MB, class Fmt>
 __device__ __forceinline__ void dispatch_tile(int mb, const Fmt &fmt, const ContigRows &rws,
                                               const uint8_t *xbase, int K, int N, int n0,
                                               uint8_t *smem, const TileLane &tl)
 {
     if constexpr (MB > 1) {
         if (mb < MB) {
-            dispatch_tile<DT, MB - 1>(mb, fmt, rws, xbase, K, N, n0, smem, tl);
+            dispatch_tile<DT, NB, MB - 1>(mb, fmt, rws, xbase, K, N, n0, smem, tl);
             return;
         }
     }
-    run_tile<DT, MB>(fmt, rws, xbase, K, N, n0, smem, tl);
+    run_tile<DT, NB, MB>(fmt, rws, xbase, K, N, n0, smem, tl);
 }
 
-// m_offsets == nullptr: dense problem of M rows (n_mt tiles of 32 * MBMAX rows).
-template <int DT, int MBMAX, bool HAS_Z>
+// m_offsets == nullptr: dense problem of M rows (n_mt tiles of TM_MAX rows).
+template <int DT, int NB, bool HAS_Z>
 __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros,
     uint16_t *__restrict__ y, const int64_t *__restrict__ m_offsets, int num_groups, int M, int N,
     int K, int gshift, int n_mt, int n_nt)
 {
-    constexpr int TMX = 32 * MBMAX;
+    using GEO = TileGeo<NB>;
+    constexpr int TMX = GEO::TM_MAX;
     extern __shared__ __align__(16) uint8_t smem[];
 
     int e = 0, m0, rows, nt;
@@ -162,34 +167,37 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
     }
     if (rows <= 0)
         return;
-    const int n0 = nt * TL_TN;
+    const int n0 = nt * GEO::TN;
     const int G = K >> (5 + gshift);
     const TileLane tl;
-    const FmtW4<DT, HAS_Z> fmt(qweight + (size_t)e * N * (K >> 3), scales + (size_t)e * N * G,
-                               HAS_Z ? qzeros + (size_t)e * (N >> 3) * G : qzeros, N, K, gshift,
-                               n0, tl);
+    const FmtW4<DT, HAS_Z, NB> fmt(qweight + (size_t)e * N * (K >> 3),
+                                   scales + (size_t)e * N * G,
+                                   HAS_Z ? qzeros + (size_t)e * (N >> 3) * G : qzeros, N, K,
+                                   gshift, n0, tl);
     ContigRows rws;
-    rws.rowb = 2u * (uint32_t)K;
-    rws.rl = tl.rl;
+    const uint32_t rowb = 2u * (uint32_t)K;
+    rws.o0 = rowb * (uint32_t)tl.rl;
+    rws.s16 = rowb * 16u;
+    rws.omax = rowb * (uint32_t)(rows - 1);
     rws.rows = rows;
     rws.y0 = y + (size_t)m0 * N;
     rws.N = N;
     const uint8_t *xbase = reinterpret_cast<const uint8_t *>(x + (size_t)m0 * K);
-    dispatch_tile<DT, MBMAX>((rows + 31) >> 5, fmt, rws, xbase, K, N, n0, smem, tl);
+    dispatch_tile<DT, NB, GEO::MB_MAX>((rows + 31) >> 5, fmt, rws, xbase, K, N, n0, smem, tl);
 }
 
-template <int DT, int MBMAX, bool HAS_Z>
+template <int DT, int NB, bool HAS_Z>
 hipError_t launch_k(const W4Args &a, const int64_t *m_offsets, int num_groups, int grid, int n_mt,
                     int n_nt, size_t lds, hipStream_t stream)
 {
     const int gshift = a.g == 32 ? 0 : a.g == 64 ? 1 : 2;
-    auto kern = w4a16_tiled_kernel<DT, MBMAX, HAS_Z>;
+    auto kern = w4a16_tiled_kernel<DT, NB, HAS_Z>;
     // More than 64 KB of dynamic LDS must be requested per kernel (gfx950 has 160 KB per CU).
     static hipError_t attr = hipErrorNotReady;
     if (attr != hipSuccess)
         attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   tile_lds_bytes(MBMAX));
+                                   TileGeo<NB>::lds_bytes(TileGeo<NB>::MB_MAX));
     if (attr != hipSuccess)
         return attr;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(TL_THREADS), lds, stream,
@@ -203,23 +211,24 @@ hipError_t launch_k(const W4Args &a, const int64_t *m_offsets, int num_groups, i
 template <int DT, bool HAS_Z>
 hipError_t launch_z(const W4Args &a, const int64_t *m_offsets, int num_groups, hipStream_t stream)
 {
-    constexpr int TMX = 32 * TL_MB_MAX;
-    const int n_nt = (a.N + TL_TN - 1) / TL_TN;
+    using GEO = TileGeo<TILED_NB>;
+    constexpr int TMX = GEO::TM_MAX;
+    const int n_nt = (a.N + GEO::TN - 1) / GEO::TN;
     if (!m_offsets) {
         // One tile row when M fits in it: size LDS for the blocks it needs.
         const int n_mt = (a.M + TMX - 1) / TMX;
-        const int mb = n_mt == 1 ? (a.M + 31) / 32 : TL_MB_MAX;
+        const int mb = n_mt == 1 ? (a.M + 31) / 32 : GEO::MB_MAX;
         const int grid = 8 * ((n_mt * n_nt + 7) / 8);
-        return launch_k<DT, TL_MB_MAX, HAS_Z>(a, nullptr, 0, grid, n_mt, n_nt,
-                                              (size_t)tile_lds_bytes(mb), stream);
+        return launch_k<DT, TILED_NB, HAS_Z>(a, nullptr, 0, grid, n_mt, n_nt,
+                                             (size_t)GEO::lds_bytes(mb), stream);
     }
     // Upper bound on the tiles of all groups: sum of ceil(rows_e / TMX).
     const int64_t max_mt = (a.M + TMX - 1) / TMX + num_groups;
     const int64_t grid = 8 * ((max_mt * n_nt + 7) / 8);
     if (grid > INT_MAX)
         return hipErrorInvalidValue;
-    return launch_k<DT, TL_MB_MAX, HAS_Z>(a, m_offsets, num_groups, (int)grid, 0, n_nt,
-                                          (size_t)tile_lds_bytes(TL_MB_MAX), stream);
+    return launch_k<DT, TILED_NB, HAS_Z>(a, m_offsets, num_groups, (int)grid, 0, n_nt,
+                                         (size_t)GEO::lds_bytes(GEO::MB_MAX), stream);
 }
 
 hipError_t launch_any(const W4Args &a, const int64_t *m_offsets, int num_groups, hipStream_t stream)

@@ -4,8 +4,8 @@
 // Mechanism (cooperative shared tile: "ROCm KQuantGemmKWmmaQ4K/Q6K: redesign
 // around a cooperative shared tile, matching llama.cpp's mul_mat_q
 // mechanism", sections Confirmed mechanism and The work): one workgroup owns
-// a 256 x TM output tile (weight rows x activation rows).  The packed weights
-// of its 256 rows are loaded and dequantized exactly once, split across the
+// a TN x TM output tile (weight rows x activation rows).  The packed weights
+// of its TN rows are loaded and dequantized exactly once, split across the
 // waves so no wave repeats another's work; one copy of the activation tile in
 // LDS serves every wave; each wave multiplies its own weight rows against the
 // whole activation range.  Dequantization and the matrix multiply are
@@ -15,11 +15,18 @@
 // gfx950 realisation:
 //  * Matrix core: v_mfma_f32_32x32x16_{f16,bf16} (32 cycles each, measured
 //    with the MFMA busy counter), so every tile is built from 32 x 32 blocks.
-//  * 4 waves; wave w owns weight rows n0 + 64 w .. +63 (two 32-row blocks nb)
-//    and all TM = 32 * MB activation rows of the tile: 2 x MB accumulator
-//    blocks of 16 fp32 registers.
+//  * 4 waves; wave w owns weight rows n0 + 32 NB w .. +32 NB - 1 (NB 32-row
+//    blocks nb) and all TM = 32 MB activation rows of the tile: NB x MB
+//    accumulator blocks of 16 fp32 registers (NB * MB <= 16, so the
+//    accumulators take at most 256 of a lane's 512 registers).  TN = 128 NB.
+//    One activation operand read from LDS feeds NB MFMAs and one dequantized
+//    weight word feeds MB, so NB trades LDS reads (measured: each read the
+//    wave issues between its MFMAs stalls the matrix pipe) for dequantization
+//    work.  NB = 4, MB = 4 (512 x 128) also moves the fewest bytes into LDS
+//    per MFMA for 4-bit weights and 16-bit activations (2 TM + TN / 2 bytes
+//    per k is smallest at TN = 4 TM).
 //  * K advances in spans of 128 (8 MFMA steps of 16).  Lane (nl, h) =
-//    (lane % 32, lane / 32) loads 32 bytes of weight row nl of each block:
+//    (lane % 32, lane / 32) takes 32 bytes of weight row nl of each block:
 //    words 8h .. 8h+7 of the span, i.e. k = 64h .. 64h+63 of the span, as two
 //    16-byte halves hf (32 k each).  MFMA step s uses word s of that load:
 //    operand slot (h, e) holds k = 64h + 8s + e.  The activation operand uses
@@ -31,21 +38,24 @@
 //    (32 rows x one block each) bank-conflict free.  Rows come from a per-lane
 //    byte offset supplied by the caller, so the same copy serves contiguous
 //    rows and gathered (routed) rows.
-//  * The packed codes of the 256 weight rows (64 bytes per row per span) are
+//  * The packed codes of the TN weight rows (64 bytes per row per span) are
 //    copied into LDS the same way, 16 rows per wave instruction, so each
 //    instruction reads sixteen contiguous 64-byte row segments instead of
 //    scattering 16-byte pieces of 32 rows (measured: the scattered per-lane
 //    code loads cost more than a fifth of the kernel).  A lane reads back its
-//    two rows' 32 bytes per span with four ds_read_b128; LDS row R keeps its
+//    NB rows' 32 bytes per span with 2 NB ds_read_b128; LDS row R keeps its
 //    16-byte piece p at position p ^ ((R >> 2) & 3), which makes those reads
 //    bank-conflict free.
 //  * Software pipeline: within a span the loop runs over the 8 MFMA steps;
-//    each step dequantizes the two weight words it needs (one per 32-row
-//    block) and issues its 2 x MB MFMAs, while the next step's activation
-//    operands are read from LDS and its two words are dequantized.  The
-//    per-row scales and zero-points are double buffered in registers and
-//    loaded a whole span ahead; the next span's activation and code tiles
-//    stream into the other LDS buffers.
+//    each step dequantizes the NB weight words it needs (one per 32-row
+//    block) and issues its NB x MB MFMAs, while the next step's activation
+//    operands are read from LDS and its words are dequantized.  The per-row
+//    scales and zero-points are double buffered in registers and loaded a
+//    whole span ahead; the next span's activation and code tiles stream into
+//    the other LDS buffers.  Those copies are issued between MFMA groups of
+//    the first steps (measured: issued in one burst at the start of the span
+//    they stalled the wave for a fifth of the loop), with scalar LDS
+//    addresses and one vector add per copy.
 //  * Tails: weight rows past the matrix are clamped to valid addresses and
 //    never stored; activation rows past the tile's row count are clamped to a
 //    valid row and never stored; a 32-wide K slice past K gets zero weights.
@@ -54,11 +64,12 @@
 // policy with:
 //    const uint8_t *wq;                   codes of row 0 of the matrix
 //    int tile_row(int n0, int N, int t) const;  matrix row of tile row t (clamped)
+//    (the policy is built for one NB and addresses rows 32 NB w + 32 nb + nl)
 //    struct Meta;                         a lane's scales / zero-points of a span
 //    static constexpr int NLOADS;         vector-memory operations per load_meta()
 //    void load_meta(int span, Meta &m) const;
-//    static constexpr bool ZERO_BY_SCALE;  slices past K zeroed through their scales
-//    void zero_past_k(int span, Meta &m) const;  scales of slices past K -> 0
+//    void zero_past_k(int span, u32x4 (&cw)[NB][2], Meta &m) const;
+//                                         weights of slices past K -> 0 (codes or scales)
 //    u32x4 dequant(uint32_t word, const Meta &m, int nb, int st) const;
 #pragma once
 
@@ -71,17 +82,27 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 
 constexpr int TL_WAVES = 4;
 constexpr int TL_THREADS = 64 * TL_WAVES;
-constexpr int TL_TN = 64 * TL_WAVES; // weight rows per workgroup
-constexpr int TL_SPAN = 128;         // K per span
-constexpr int TL_ROWB = 256;         // LDS bytes per activation row of a span
-constexpr int TL_MB_MAX = 8;         // largest tile: 256 activation rows
+constexpr int TL_SPAN = 128; // K per span
+constexpr int TL_ROWB = 256; // LDS bytes per activation row of a span
 
-// LDS bytes of a tile with up to mb_max 32-row blocks (two span buffers).
-constexpr int TL_WBUF = TL_TN * 64; // LDS bytes of one span's code tile
-__host__ __device__ constexpr int tile_lds_bytes(int mb_max)
-{
-    return 2 * 32 * mb_max * TL_ROWB + 2 * TL_WBUF;
-}
+// Tile geometry for NB weight blocks per wave.
+template <int NB>
+struct TileGeo {
+    static_assert(NB == 2 || NB == 4, "weight blocks per wave");
+    static constexpr int TN = 32 * NB * TL_WAVES; // weight rows per tile
+    static constexpr int MB_MAX = 16 / NB;        // activation blocks per tile, at most
+    static constexpr int TM_MAX = 32 * MB_MAX;
+    static constexpr int WBUF = TN * 64;          // LDS bytes of one span's code tile
+    static constexpr int WDMA = TN / 64;          // code copies per wave per span
+    // LDS bytes of a tile with mb 32-row blocks: two span buffers of each
+    // operand, or the epilogue's staging of the output tile if larger.
+    __host__ __device__ static constexpr int lds_bytes(int mb)
+    {
+        const int main = 2 * 32 * mb * TL_ROWB + 2 * WBUF;
+        const int stage = 32 * mb * (2 * TN + 16);
+        return main > stage ? main : stage;
+    }
+};
 
 // s_waitcnt that waits until at most `n` vector-memory operations are
 // outstanding (expcnt and lgkmcnt left alone; gfx9 encoding).
@@ -144,7 +165,7 @@ struct TileLane {
     int xblk; // 16-byte block of that row this lane copies
     __device__ TileLane()
     {
-        wave = threadIdx.x >> 6;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // uniform: scalar LDS addresses
         lane = threadIdx.x & 63;
         nl = lane & 31;
         h = lane >> 5;
@@ -158,55 +179,65 @@ struct TileLane {
 // tile, already clamped to a valid row:  uint32_t XRows::off(int i) const
 // returns the offset of row 16 i + rl for this lane.
 //
-// The tile body: runs the whole K loop for one 256 x (32 MB) tile and leaves
-// the accumulators in `acc`.  `Fmt` holds this lane's weight addressing.
-template <int DT, int MB, class Fmt, class XRows>
+// The tile body: runs the whole K loop for one (128 NB) x (32 MB) tile and
+// leaves the accumulators in `acc`.  `Fmt` holds this lane's weight
+// addressing.
+template <int DT, int NB, int MB, class Fmt, class XRows>
 __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
                                               const uint8_t *xbase, int K, int n0, int N,
                                               uint8_t *smem, const TileLane &tl,
-                                              float16_t (&acc)[2][MB])
+                                              float16_t (&acc)[NB][MB])
 {
+    using GEO = TileGeo<NB>;
+    static_assert(MB >= 1 && MB <= GEO::MB_MAX, "accumulator budget");
     constexpr int TM = 32 * MB;
+    constexpr int WD = GEO::WDMA;
     const int S = (K + TL_SPAN - 1) / TL_SPAN;
     const uint32_t lds0 = (uint32_t)(size_t)(lds_ptr_t *)smem;
     const uint32_t wlds0 = lds0 + (uint32_t)(2 * TM * TL_ROWB);
     const uint8_t *wsm = smem + 2 * TM * TL_ROWB;
 
-    // Code tile DMA: 256 rows x 64 bytes per span, 16 rows (1 KB) per wave
-    // instruction, instructions 4 w .. 4 w + 3 for wave w.  Lane L writes row
-    // L / 4 of the instruction's 16 at position L % 4, so it copies piece
-    // (L % 4) ^ (L / 16) of that row.  Rows past N are clamped (never stored);
-    // pieces past the end of a row are clamped inside it (zeroed at dequant).
+    // Code tile DMA: TN rows x 64 bytes per span, 16 rows (1 KB) per wave
+    // instruction, instructions WD w .. WD w + WD - 1 for wave w (WD = TN / 64).
+    // Lane L writes row L / 4 of the instruction's 16 at position L % 4, so it
+    // copies piece (L % 4) ^ (L / 16) of that row.  Rows past N are clamped
+    // (never stored); pieces past the end of a row are clamped inside it
+    // (zeroed at dequant).
     const uint32_t rowb = (uint32_t)K >> 1;
-    uint32_t crow[4];
+    uint32_t crow[WD];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-        crow[jj] = (uint32_t)fmt.tile_row(n0, N, 16 * (4 * tl.wave + jj) + (tl.lane >> 2)) * rowb;
+    for (int jj = 0; jj < WD; ++jj)
+        crow[jj] = (uint32_t)fmt.tile_row(n0, N, 16 * (WD * tl.wave + jj) + (tl.lane >> 2)) * rowb;
     const uint32_t cpiece = 16u * (uint32_t)((tl.lane & 3) ^ (tl.lane >> 4));
-    auto issue_w = [&](int span, int buf) __attribute__((always_inline)) {
-        const uint32_t kb = min((uint32_t)span * 64u + cpiece, rowb - 16u);
-        const uint32_t dst = wlds0 + (uint32_t)(buf * TL_WBUF + 4 * tl.wave * 1024);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            lds_dma16(fmt.wq, crow[jj] + kb, __builtin_amdgcn_readfirstlane(dst + 1024u * jj));
-    };
 
     // Activation tile DMA: TM rows x 16 blocks per span, 1 KB per wave
     // instruction.  Instruction i of wave w fills LDS rows 16 i + 4 w .. +3;
     // lane L takes row 16 i + rl and position L % 16, which holds global block
     // (L % 16) ^ rl of that row.  Blocks past K are clamped inside the row
     // (they meet zero weights).
-    auto issue_x = [&](int span, int buf) __attribute__((always_inline)) {
-        const uint32_t ldsb = lds0 + (uint32_t)(buf * TM * TL_ROWB);
-        const uint32_t kb = 2u * (uint32_t)min(span * TL_SPAN + 8 * tl.xblk, K - 8);
-#pragma unroll
-        for (int i = 0; i < TM / 16; ++i)
-            lds_dma16(xbase, xr.off(i) + kb,
-                      __builtin_amdgcn_readfirstlane(ldsb + (uint32_t)((16 * i + 4 * tl.wave) * TL_ROWB)));
+    //
+    // Copy d of a span (d < 2 MB: activation instruction d, else code
+    // instruction d - 2 MB).  The per-span lane offsets kx / kw are computed
+    // once per span; LDS addresses are wave-uniform (scalar).
+    constexpr int ND = TM / 16 + WD;
+    auto dma = [&](int d, int buf, uint32_t kx, uint32_t kw) __attribute__((always_inline)) {
+        if (d < TM / 16) {
+            const uint32_t ldsb = lds0 + (uint32_t)(buf * TM * TL_ROWB);
+            lds_dma16(xbase, xr.off(d) + kx,
+                      ldsb + (uint32_t)((16 * d + 4 * tl.wave) * TL_ROWB));
+        } else {
+            const int jj = d - TM / 16;
+            lds_dma16(fmt.wq, crow[jj] + kw,
+                      wlds0 + (uint32_t)(buf * GEO::WBUF + (WD * tl.wave + jj) * 1024));
+        }
+    };
+    auto koff = [&](int span, uint32_t &kx, uint32_t &kw) __attribute__((always_inline)) {
+        kx = 2u * (uint32_t)min(span * TL_SPAN + 8 * tl.xblk, K - 8);
+        kw = min((uint32_t)span * 64u + cpiece, rowb - 16u);
     };
 
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -218,31 +249,48 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
     typename Fmt::Meta mA, mB;
     fmt.load_meta(0, mA);
     fmt.load_meta(min(1, S - 1), mB);
-    issue_x(0, 0);
-    issue_w(0, 0);
+    {
+        uint32_t kx, kw;
+        koff(0, kx, kw);
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+            dma(d, 0, kx, kw);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     barrier_only();
+
+    // MFMAs of one step in GR groups; after group g of step st comes copy
+    // GR st + g of the next span (all ND copies land in the first steps), so
+    // the copies are spread between MFMAs instead of issued in one burst.
+    constexpr int NM = NB * MB;
+    constexpr int GR = NM < 4 ? NM : 4; // group g: MFMAs [g NM / GR, (g + 1) NM / GR)
 
     // One span: MFMAs on LDS buffers span & 1 with the scales in `cur`.  At
     // entry the next span's scales (the other buffer) have landed or are in
     // flight; this span's `cur` is refilled for span + 2 once consumed.
     auto run_span = [&](int span, typename Fmt::Meta &cur) __attribute__((always_inline)) {
         const int buf = span & 1;
-        issue_x(min(span + 1, S - 1), buf ^ 1);
-        issue_w(min(span + 1, S - 1), buf ^ 1);
+        // The next span's tiles (the last span copies itself again: no branch
+        // splits the step, and the copy is waited for before the last barrier).
+        uint32_t kx, kw;
+        koff(min(span + 1, S - 1), kx, kw);
         const uint8_t *xb = smem + (size_t)buf * TM * TL_ROWB;
-        // This lane's packed codes of the span: rows 64 w + 32 nb + nl, pieces
-        // 2 h + hf (k = 64 h + 32 hf .. +31 of the span).
-        const uint8_t *wb = wsm + buf * TL_WBUF;
-        u32x4 cw[2][2];
+        // This lane's packed codes of the span: rows 32 NB w + 32 nb + nl,
+        // pieces 2 h + hf (k = 64 h + 32 hf .. +31 of the span).
+        const uint8_t *wb = wsm + buf * GEO::WBUF;
+        u32x4 cw[NB][2];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const int R = 64 * tl.wave + 32 * nb + tl.nl;
+                const int R = 32 * NB * tl.wave + 32 * nb + tl.nl;
                 const int pos = (2 * tl.h + hf) ^ ((tl.nl >> 2) & 3);
                 cw[nb][hf] = *reinterpret_cast<const u32x4 *>(wb + R * 64 + 16 * pos);
             }
+        // Only a span that crosses K (uniform test) has slices past K; the
+        // format zeroes their weights once (codes or scales).
+        if (span * TL_SPAN + TL_SPAN > K)
+            fmt.zero_past_k(span, cw, cur);
         // Activation operand of block mb, step st: 32 rows (nl), 16-byte
         // block 8h + st of the span.
         auto read_x = [&](int mb, int st) __attribute__((always_inline)) {
@@ -250,27 +298,12 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
             const int p = (8 * tl.h + st) ^ (R & 15);
             return *reinterpret_cast<const u32x4 *>(xb + R * TL_ROWB + 16 * p);
         };
-        // Only a span that crosses K (uniform test) has slices past K.  Their
-        // weights become zero: through zero scales (one select per slice), or
-        // per operand word (one select per word), whichever the format's
-        // kernel measured faster (the choice changes the compiler's register
-        // allocation of the whole loop).
-        const bool ktail = span * TL_SPAN + TL_SPAN > K;
-        if constexpr (Fmt::ZERO_BY_SCALE) {
-            if (ktail)
-                fmt.zero_past_k(span, cur);
-        }
         auto dq = [&](int nb, int st) __attribute__((always_inline)) {
-            u32x4 v = fmt.dequant(cw[nb][st >> 2][st & 3], cur, nb, st);
-            if constexpr (!Fmt::ZERO_BY_SCALE) {
-                if (ktail && span * TL_SPAN + 64 * tl.h + 32 * (st >> 2) >= K)
-                    v = u32x4{0, 0, 0, 0};
-            }
-            return v;
+            return fmt.dequant(cw[nb][st >> 2][st & 3], cur, nb, st);
         };
-        u32x4 wc[2], wn[2], xc[MB], xn[MB];
+        u32x4 wc[NB], wn[NB], xc[MB], xn[MB];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
             wc[nb] = dq(nb, 0);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -282,18 +315,25 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
                 for (int mb = 0; mb < MB; ++mb)
                     xn[mb] = read_x(mb, st + 1);
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < NB; ++nb)
                     wn[nb] = dq(nb, st + 1);
             }
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+            for (int g = 0; g < GR; ++g) {
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    acc[nb][mb] = mfma32x32x16<DT>(wc[nb], xc[mb], acc[nb][mb]);
+                for (int j = g * NM / GR; j < (g + 1) * NM / GR; ++j)
+                    acc[j % NB][j / NB] =
+                        mfma32x32x16<DT>(wc[j % NB], xc[j / NB], acc[j % NB][j / NB]);
+                if (GR * st + g < ND) {
+                    dma(GR * st + g, buf ^ 1, kx, kw);
+                    // MFMAs stay in their group; other work may cross
+                    __builtin_amdgcn_sched_barrier(0x0002 | 0x0004 | 0x0100);
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
             if (st < 7) {
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < NB; ++nb)
                     wc[nb] = wn[nb];
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
@@ -329,21 +369,23 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
 // activation-dtype values (row stride padded by 16 bytes against bank
 // conflicts) in the LDS the main loop has released.  `yr.row(r)` returns the
 // output row pointer of tile row r, called only for r < rows.
-template <int DT, int MB, class YRows>
-__device__ __forceinline__ void tile_store(const float16_t (&acc)[2][MB], const YRows &yr, int rows,
-                                          int n0, int N, const TileLane &tl, uint8_t *smem)
+template <int DT, int NB, int MB, class YRows>
+__device__ __forceinline__ void tile_store(const float16_t (&acc)[NB][MB], const YRows &yr,
+                                          int rows, int n0, int N, const TileLane &tl,
+                                          uint8_t *smem)
 {
+    constexpr int TN = TileGeo<NB>::TN;
     constexpr int TM = 32 * MB;
-    constexpr int RS = TL_TN * 2 + 16; // LDS bytes per staged row
-    static_assert(TM * RS <= 2 * TM * TL_ROWB + 2 * TL_WBUF, "staging fits the tile's LDS");
+    constexpr int RS = TN * 2 + 16; // LDS bytes per staged row
+    static_assert(TM * RS <= TileGeo<NB>::lds_bytes(MB), "staging fits the tile's LDS");
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int m = 32 * mb + tl.nl;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                const int c = 64 * tl.wave + 32 * nb + 8 * g4 + 4 * tl.h;
+                const int c = 32 * NB * tl.wave + 32 * nb + 8 * g4 + 4 * tl.h;
                 const float16_t &v = acc[nb][mb];
                 uint2 o;
                 o.x = f32x2_to_act2<DT>(v[4 * g4 + 0], v[4 * g4 + 1]);
@@ -353,10 +395,11 @@ __device__ __forceinline__ void tile_store(const float16_t (&acc)[2][MB], const 
         }
     }
     __syncthreads();
-    // 32 chunks of 16 bytes (8 values) per staged row; N % 8 == 0, so a chunk
-    // is either wholly inside the matrix or wholly past it.
-    for (int i = threadIdx.x; i < TM * 32; i += TL_THREADS) {
-        const int r = i >> 5, c = i & 31;
+    // TN / 8 chunks of 16 bytes (8 values) per staged row; N % 8 == 0, so a
+    // chunk is either wholly inside the matrix or wholly past it.
+    constexpr int CPR = TN / 8;
+    for (int i = threadIdx.x; i < TM * CPR; i += TL_THREADS) {
+        const int r = i / CPR, c = i % CPR;
         const int n = n0 + 8 * c;
         if (r < rows && n < N)
             *reinterpret_cast<u32x4 *>(yr.row(r) + n) =
@@ -365,39 +408,44 @@ __device__ __forceinline__ void tile_store(const float16_t (&acc)[2][MB], const 
 }
 
 // Store with the fused stage-1 activation (paired layout, see FmtFP4): the
-// same accumulator register of blocks nb = 0 and 1 holds gate and up of one
-// output column, n = n0 + 32 w + 8 g4 + 4 h + j, so out = silu(gate) * up in
-// fp32 with silu(v) = v / (1 + e^-v), rounded once to the activation dtype.
-// Staged through LDS as for tile_store: 128 output columns per tile row.
-template <int DT, int MB, class YRows>
-__device__ __forceinline__ void tile_store_silu_mul(const float16_t (&acc)[2][MB], const YRows &yr,
-                                                   int rows, int n0, int I, const TileLane &tl,
-                                                   uint8_t *smem)
+// same accumulator register of blocks nb = 2 p and 2 p + 1 holds gate and up
+// of one output column, n = n0 + 16 NB w + 32 p + 8 g4 + 4 h + j, so
+// out = silu(gate) * up in fp32 with silu(v) = v / (1 + e^-v), rounded once
+// to the activation dtype.  Staged through LDS as for tile_store: TN / 2
+// output columns per tile row.
+template <int DT, int NB, int MB, class YRows>
+__device__ __forceinline__ void tile_store_silu_mul(const float16_t (&acc)[NB][MB],
+                                                   const YRows &yr, int rows, int n0, int I,
+                                                   const TileLane &tl, uint8_t *smem)
 {
+    constexpr int TN = TileGeo<NB>::TN;
     constexpr int TM = 32 * MB;
-    constexpr int RS = TL_TN + 16; // LDS bytes per staged row (128 values + pad)
+    constexpr int RS = TN + 16; // LDS bytes per staged row (TN / 2 values + pad)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int m = 32 * mb + tl.nl;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const int c = 32 * tl.wave + 8 * g4 + 4 * tl.h;
-            float o4[4];
+        for (int p = 0; p < NB / 2; ++p)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float g = acc[0][mb][4 * g4 + j];
-                const float u = acc[1][mb][4 * g4 + j];
-                o4[j] = g / (1.0f + expf(-g)) * u;
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int c = 16 * NB * tl.wave + 32 * p + 8 * g4 + 4 * tl.h;
+                float o4[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float g = acc[2 * p][mb][4 * g4 + j];
+                    const float u = acc[2 * p + 1][mb][4 * g4 + j];
+                    o4[j] = g / (1.0f + expf(-g)) * u;
+                }
+                uint2 o;
+                o.x = f32x2_to_act2<DT>(o4[0], o4[1]);
+                o.y = f32x2_to_act2<DT>(o4[2], o4[3]);
+                *reinterpret_cast<uint2 *>(smem + m * RS + 2 * c) = o;
             }
-            uint2 o;
-            o.x = f32x2_to_act2<DT>(o4[0], o4[1]);
-            o.y = f32x2_to_act2<DT>(o4[2], o4[3]);
-            *reinterpret_cast<uint2 *>(smem + m * RS + 2 * c) = o;
-        }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < TM * 16; i += TL_THREADS) {
-        const int r = i >> 4, c = i & 15;
+    constexpr int CPR = TN / 16;
+    for (int i = threadIdx.x; i < TM * CPR; i += TL_THREADS) {
+        const int r = i / CPR, c = i % CPR;
         const int n = n0 + 8 * c;
         if (r < rows && n < I)
             *reinterpret_cast<u32x4 *>(yr.row(r) + n) =
@@ -435,17 +483,16 @@ __device__ __forceinline__ int xcd_tile(int tiles)
 
 // W4A16: packed codes qweight[N][K/8], scales[N][K/g] in DT, packed
 // zero-points qzeros[N/8][K/g] (or none: z = 8).  Each lane handles rows
-// n_nb = n0 + 64 wave + 32 nb + nl, which share n % 8, so one nibble shift of
-// the zero-point words serves both blocks.
-template <int DT, bool HAS_Z>
+// n_nb = n0 + 32 NB wave + 32 nb + nl, which share n % 8, so one nibble shift
+// of the zero-point words serves all its blocks.
+template <int DT, bool HAS_Z, int NB>
 struct FmtW4 {
-    static constexpr int NLOADS = HAS_Z ? 8 : 4;
-    static constexpr bool ZERO_BY_SCALE = true;
+    static constexpr int NLOADS = NB * (HAS_Z ? 4 : 2);
     struct Meta {
-        uint32_t s[2][2], z[2][2];
+        uint32_t s[NB][2], z[NB][2];
     };
     const uint8_t *wq, *ws, *wz;
-    uint32_t soff[2], zoff[2];
+    uint32_t soff[NB], zoff[NB];
     int K, gshift, h, zsh;
 
     __device__ FmtW4(const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
@@ -460,8 +507,8 @@ struct FmtW4 {
         zsh = 4 * (tl.nl & 7);
         const int G = K >> (5 + gshift);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int n = min(n0 + 64 * tl.wave + 32 * nb + tl.nl, N - 1);
+        for (int nb = 0; nb < NB; ++nb) {
+            const int n = min(n0 + 32 * NB * tl.wave + 32 * nb + tl.nl, N - 1);
             soff[nb] = (uint32_t)n * (uint32_t)G * 2u;
             zoff[nb] = (uint32_t)(n >> 3) * (uint32_t)G * 4u;
         }
@@ -477,7 +524,7 @@ struct FmtW4 {
             const int kc = min(k, K - 32); // slice past K: clamped load, scale zeroed at use
             const uint32_t grp = (uint32_t)(kc >> (5 + gshift));
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
+            for (int nb = 0; nb < NB; ++nb) {
                 m.s[nb][hf] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + 2u * grp);
                 m.z[nb][hf] = HAS_Z ? *reinterpret_cast<const uint32_t *>(wz + zoff[nb] + 4u * grp)
                                     : 0x88888888u;
@@ -485,14 +532,15 @@ struct FmtW4 {
         }
     }
 
-    __device__ __forceinline__ void zero_past_k(int span, Meta &m) const
+    // Slices past K: zero scales ((q - z) * 0 is a zero of either sign).
+    __device__ __forceinline__ void zero_past_k(int span, u32x4 (&)[NB][2], Meta &m) const
     {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
             if (span * TL_SPAN + 64 * h + 32 * hf >= K)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    m.s[nb][hf] = 0u; // (q - z) * 0 is a zero of either sign
+                for (int nb = 0; nb < NB; ++nb)
+                    m.s[nb][hf] = 0u;
     }
 
     __device__ __forceinline__ u32x4 dequant(uint32_t word, const Meta &m, int nb, int st) const
@@ -508,19 +556,18 @@ struct FmtW4 {
 // one aligned 16-bit scale load.
 //
 // Paired layout (PAIRED, for the fused gate/up activation): the tile's
-// weight rows come in pairs, gate row j and up row N/2 + j, so that
-// block nb = 0 of wave w holds gate rows n0 + 32 w .. +31 and block nb = 1
-// the matching up rows; tile row t = 64 w + 32 nb + i maps to matrix row
-// nb * N/2 + n0 + 32 w + i.
-template <bool PAIRED>
+// weight rows come in pairs, gate row j and up row N/2 + j, so that block
+// nb = 2 p of wave w holds gate rows n0 + 16 NB w + 32 p .. +31 and block
+// 2 p + 1 the matching up rows; tile row t = 32 NB w + 32 nb + i maps to
+// matrix row (nb % 2) * N/2 + n0 + 16 NB w + 32 (nb / 2) + i.
+template <bool PAIRED, int NB>
 struct FmtFP4 {
-    static constexpr int NLOADS = 2;
-    static constexpr bool ZERO_BY_SCALE = false;
+    static constexpr int NLOADS = NB;
     struct Meta {
-        uint32_t s[2]; // E8M0 bytes of slices hf = 0 (low byte) and 1
+        uint32_t s[NB]; // E8M0 bytes of slices hf = 0 (low byte) and 1
     };
     const uint8_t *wq, *ws;
-    uint32_t soff[2];
+    uint32_t soff[NB];
     int K, h;
 
     __device__ FmtFP4(const uint8_t *w_fp4, const uint8_t *w_scale, int N, int K_, int n0,
@@ -531,21 +578,23 @@ struct FmtFP4 {
         K = K_;
         h = tl.h;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int n = tile_row(n0, N, 64 * tl.wave + 32 * nb + tl.nl);
+        for (int nb = 0; nb < NB; ++nb) {
+            const int n = tile_row(n0, N, 32 * NB * tl.wave + 32 * nb + tl.nl);
             soff[nb] = (uint32_t)n * (uint32_t)(K >> 5);
         }
     }
 
-    // Matrix row of tile row t; PAIRED: t = 64 w + 32 nb + i is row
-    // nb * N/2 + n0 + 32 w + i (gate rows, then the matching up rows).
+    // Matrix row of tile row t; PAIRED: t = 32 NB w + 32 nb + i is row
+    // (nb % 2) * N/2 + n0 + 16 NB w + 32 (nb / 2) + i (gate rows, then the
+    // matching up rows).
     __device__ __forceinline__ int tile_row(int n0, int N, int t) const
     {
         if constexpr (!PAIRED) {
             return min(n0 + t, N - 1);
         } else {
             const int half = N >> 1;
-            return ((t >> 5) & 1) * half + min(n0 + 32 * (t >> 6) + (t & 31), half - 1);
+            const int w = t / (32 * NB), nb = (t >> 5) % NB;
+            return (nb & 1) * half + min(n0 + 16 * NB * w + 32 * (nb >> 1) + (t & 31), half - 1);
         }
     }
 
@@ -554,18 +603,20 @@ struct FmtFP4 {
         const int k = min(span * TL_SPAN + 64 * h, K - 64); // past K: clamped, zeroed later
         const uint32_t kg = (uint32_t)k >> 5;               // even
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
             m.s[nb] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + kg);
     }
 
-    __device__ __forceinline__ void zero_past_k(int span, Meta &m) const
+    // Slices past K: zero codes (E2M1 code 0 is +0).  K % 64 == 0, so both
+    // 32-wide slices of a lane are inside K or both past it.
+    __device__ __forceinline__ void zero_past_k(int span, u32x4 (&cw)[NB][2], Meta &) const
     {
-        // K % 64 == 0: both 32-wide slices of a lane are inside K or past it;
-        // E8M0 byte 0 becomes the scale 0.0 (see e8m0_to_f32)
         if (span * TL_SPAN + 64 * h >= K)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-                m.s[nb] = 0u;
+            for (int nb = 0; nb < NB; ++nb) {
+                cw[nb][0] = u32x4{0u, 0u, 0u, 0u};
+                cw[nb][1] = u32x4{0u, 0u, 0u, 0u};
+            }
     }
 
     __device__ __forceinline__ u32x4 dequant(uint32_t word, const Meta &m, int nb, int st) const
