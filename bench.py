@@ -17,8 +17,9 @@ graph the kernels run back to back, so the step time is the kernel's average
 launch duration and the roofline entry uses it.  The CPU baseline is the
 oracle (single-threaded C) on the full decode call.
 
-Other workloads of the pages (tiny GEMV, small batch, prefill, MoE stage 1)
-are measured the same way and reported under "others".
+Other workloads of the pages (tiny GEMV, small batch, prefill, MoE stage 1,
+the zero-point page's qkv / down decode shapes and batch-4 g = 128 shapes) are
+measured the same way and reported under "others".
 """
 from __future__ import annotations
 
@@ -290,7 +291,7 @@ def main():
         line["cpu_baseline"] = None
     if not args.no_others:
         others = {}
-        for w in wl.WORKLOADS:
+        for w in wl.WORKLOADS + wl.EXTRA_WORKLOADS:
             if w.key == head.key:
                 continue
             try:

@@ -105,6 +105,30 @@ def test_config_decode_gemv_full_size(wob, oracle):
     assert ok, (err, bound)
 
 
+@pytest.mark.parametrize("key", ["bs4_2048x2560", "bs4_6144x2048", "bs4_4096x2048"])
+def test_page_batch4_shapes(wob, oracle, key):
+    """The zero-point page's batch-4, g = 128 asymmetric shapes, every output."""
+    d = wl.BY_KEY[key].make()
+    _check(oracle, d, _run(wob, d, wob.PATH_AUTO))
+
+
+@pytest.mark.parametrize("key", ["decode_qkv", "decode_down"])
+def test_page_decode_shapes_full_size(wob, oracle, key):
+    """The page's qkv and down decode shapes at full size: every output finite,
+    2048 sampled outputs (including both ends) against the oracle."""
+    d = wl.BY_KEY[key].make()
+    ybits = _run(wob, d, wob.PATH_AUTO, sentinel=True)
+    y = oracle.act_decode(ybits, d["dtype"])
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(1)
+    ns = np.unique(np.concatenate([[0, 1, 7, 8, d["N"] - 1], rng.integers(0, d["N"], 2048)]))
+    ms = np.zeros_like(ns)
+    yref = oracle.w4a16_gemm_sampled(d["x"], d["dtype"], d["qweight"], d["scales"], d["qzeros"],
+                                     d["K"], d["g"], ms, ns)
+    ok, err, bound = oracle.tolerance_ok(y[ms, ns], yref)
+    assert ok, (err, bound)
+
+
 def test_refuses_act_dtype_zero_points(wob):
     torch = torch_mod()
     d = wl.w4a16_inputs(1, 16, 64, 32, wl.F16)

@@ -6,35 +6,45 @@
 //
 // Two kernels on the caller's stream:
 //  1. Routing (one workgroup): histogram of the expert ids in LDS, prefix sums
-//     of the rows and of the 128-row tiles per expert, a tile table
+//     of the rows and of the TM-row tiles per expert, a tile table
 //     {expert, first sorted row, rows} and the pairs sorted by expert (order
 //     inside an expert is arbitrary; every output row is computed the same
 //     way wherever it sits in a tile).  Ids outside [0, E) form one extra
 //     "expert" whose tiles write zero rows.
 //  2. Grouped MFMA GEMM: the cooperative-tile pipeline of wob_tile.hpp with the
-//     MXFP4 weight format.  A workgroup takes one (expert tile, 512 weight
-//     rows) pair; its activation rows are gathered from x by token, the FP4
+//     MXFP4 weight format.  A workgroup takes one (expert tile, weight-row
+//     tile) pair; its activation rows are gathered from x by token, the FP4
 //     words are expanded to bfloat16 with v_cvt_scalef32_pk_bf16_fp4 (one
 //     conversion per byte, two elements each, the E8M0 byte placed in the
 //     binary32 exponent as the scale), v_mfma_f32_32x32x16_bf16 multiplies,
 //     and the epilogue scatters rows to their pair index.  Stores are guarded
 //     by the tile's row count and by N, so a tile that overhangs the weight
-//     rows (N not a multiple of 512) never writes into neighbouring cells: the
-//     failure the page's store guard fixes.
+//     rows (N not a multiple of the tile) never writes into neighbouring
+//     cells: the failure the page's store guard fixes.
 //
-// An expert's rows form one tile when there are at most 128 of them (the
-// average expert of a 1024-token, 32-expert, top-4 batch), so its weights are
-// dequantized once; the tile multiplies only the 32-row blocks its row count
-// needs.
+// Tiles: 384 weight rows x up to 160 activation rows for the pre-activation
+// output, 256 x 256 for the fused activation (see moe_nb).  An expert's rows
+// form one tile when they fit (the average expert of a 1024-token, 32-expert,
+// top-4 batch has 128), so its weights stream from memory once; the tile
+// multiplies only the 32-row blocks its row count needs.
 #include "wob_internal.hpp"
 #include "wob_tile.hpp"
 
 namespace wob {
 namespace {
 
-constexpr int MOE_NB = 2;                           // weight blocks per wave
-constexpr int MOE_TM = TileGeo<MOE_NB>::TM_MAX;     // rows per expert tile
-constexpr int MOE_TN = TileGeo<MOE_NB>::TN;         // weight rows per tile
+// Weight blocks per wave: 3 (384-row weight tiles, up to 160 activation
+// rows) for the pre-activation output, whose per-span fixed costs (barrier,
+// scale loads, code copies) then spread over 1.5x the MFMAs of a 256-row tile
+// at the ~128 rows of a typical expert; 2 (256 rows, up to 256 activation
+// rows) for the fused gate / up activation, which pairs weight blocks.
+template <bool ACT>
+constexpr int moe_nb() { return ACT ? 2 : 3; }
+template <bool ACT>
+constexpr int moe_tm() { return TileGeo<moe_nb<ACT>()>::TM_MAX; } // rows per expert tile
+template <bool ACT>
+constexpr int moe_tn() { return TileGeo<moe_nb<ACT>()>::TN; } // weight rows per tile
+constexpr int MOE_TM_MIN = moe_tm<false>() < moe_tm<true>() ? moe_tm<false>() : moe_tm<true>();
 constexpr int ROUTE_THREADS = 1024;
 
 struct MoeWs {
@@ -43,7 +53,9 @@ struct MoeWs {
     int32_t *sorted; // pair indices grouped by expert
 };
 
-size_t max_tiles(int64_t P, int64_t E) { return (size_t)(P / MOE_TM + E + 2); }
+// Expert tiles of any launch: sum over experts (and the invalid-id bucket) of
+// ceil(rows / TM) <= P / TM + E + 1, for the smaller TM.
+size_t max_tiles(int64_t P, int64_t E) { return (size_t)(P / MOE_TM_MIN + E + 2); }
 
 MoeWs carve(void *ws, int64_t P, int64_t E)
 {
@@ -82,7 +94,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int *wsum, int &total)
 }
 
 __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const int32_t *__restrict__ ids,
-                                                                  int P, int E, int32_t *hdr,
+                                                                  int P, int E, int tm, int32_t *hdr,
                                                                   int4 *tiles, int32_t *sorted)
 {
     extern __shared__ int lds_i[];
@@ -110,7 +122,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const int32_t 
     int srows = 0, stiles = 0;
     for (int e = e0; e < e1; ++e) {
         srows += cnt[e];
-        stiles += (cnt[e] + MOE_TM - 1) / MOE_TM;
+        stiles += (cnt[e] + tm - 1) / tm;
     }
     int total_rows, total_tiles;
     int rb = block_excl_scan(srows, wsum, total_rows);
@@ -119,7 +131,7 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const int32_t 
         off[e] = rb;
         toff[e] = tb;
         rb += cnt[e];
-        tb += (cnt[e] + MOE_TM - 1) / MOE_TM;
+        tb += (cnt[e] + tm - 1) / tm;
     }
     if (tid == 0)
         hdr[0] = total_tiles;
@@ -127,8 +139,8 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const int32_t 
 
     for (int e = tid; e <= E; e += ROUTE_THREADS) {
         const int c = cnt[e];
-        for (int j = 0; j * MOE_TM < c; ++j)
-            tiles[toff[e] + j] = int4{e, off[e] + j * MOE_TM, min(MOE_TM, c - j * MOE_TM), 0};
+        for (int j = 0; j * tm < c; ++j)
+            tiles[toff[e] + j] = int4{e, off[e] + j * tm, min(tm, c - j * tm), 0};
     }
     __syncthreads();
     for (int e = tid; e <= E; e += ROUTE_THREADS)
@@ -159,7 +171,7 @@ struct GatherRows {
 // fused silu(gate) * up store (I = N / 2 output columns), else the plain
 // pre-activation store.
 template <bool ACT, int MB>
-__device__ __forceinline__ void moe_run(const FmtFP4<ACT, MOE_NB> &fmt, const int32_t *pairs,
+__device__ __forceinline__ void moe_run(const FmtFP4<ACT, moe_nb<ACT>()> &fmt, const int32_t *pairs,
                                         int rows, int topk, const uint16_t *x, uint16_t *y, int K,
                                         int N, int n0, uint8_t *smem, const TileLane &tl)
 {
@@ -172,17 +184,18 @@ __device__ __forceinline__ void moe_run(const FmtFP4<ACT, MOE_NB> &fmt, const in
         const int p = pairs[min(16 * i + tl.rl, rows - 1)];
         g.xo[i] = (uint32_t)(p / topk) * (uint32_t)K * 2u;
     }
-    float16_t acc[MOE_NB][MB];
-    tile_mainloop<DT_BF16, MOE_NB, MB>(fmt, g, reinterpret_cast<const uint8_t *>(x), K, n0, N,
+    constexpr int NB = moe_nb<ACT>();
+    float16_t acc[NB][MB];
+    tile_mainloop<DT_BF16, NB, MB>(fmt, g, reinterpret_cast<const uint8_t *>(x), K, n0, N,
                                        smem, tl, acc);
     if constexpr (ACT)
-        tile_store_silu_mul<DT_BF16, MOE_NB, MB>(acc, g, rows, n0, N / 2, tl, smem);
+        tile_store_silu_mul<DT_BF16, NB, MB>(acc, g, rows, n0, N / 2, tl, smem);
     else
-        tile_store<DT_BF16, MOE_NB, MB>(acc, g, rows, n0, N, tl, smem);
+        tile_store<DT_BF16, NB, MB>(acc, g, rows, n0, N, tl, smem);
 }
 
 template <bool ACT, int MB>
-__device__ __forceinline__ void moe_dispatch(int mb, const FmtFP4<ACT, MOE_NB> &fmt,
+__device__ __forceinline__ void moe_dispatch(int mb, const FmtFP4<ACT, moe_nb<ACT>()> &fmt,
                                              const int32_t *pairs, int rows, int topk,
                                              const uint16_t *x, uint16_t *y, int K, int N, int n0,
                                              uint8_t *smem, const TileLane &tl)
@@ -212,7 +225,8 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
     const int4 *__restrict__ tiles, const int32_t *__restrict__ sorted, int topk, int E, int N,
     int K, int n_nt)
 {
-    constexpr int TW = ACT ? MOE_TN / 2 : MOE_TN; // output columns per tile
+    constexpr int NB = moe_nb<ACT>();
+    constexpr int TW = ACT ? moe_tn<ACT>() / 2 : moe_tn<ACT>(); // output columns per tile
     extern __shared__ __align__(16) uint8_t smem[];
     const int t = xcd_tile(hdr[0] * n_nt);
     if (t < 0)
@@ -228,10 +242,37 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
         return;
     }
     const TileLane tl;
-    const FmtFP4<ACT, MOE_NB> fmt(w_fp4 + (size_t)e * N * (K >> 1),
+    const FmtFP4<ACT, NB> fmt(w_fp4 + (size_t)e * N * (K >> 1),
                                   w_scale + (size_t)e * N * (K >> 5), N, K, n0, tl);
-    moe_dispatch<ACT, TileGeo<MOE_NB>::MB_MAX>((rows + 31) >> 5, fmt, pairs, rows, topk, x, y, K,
+    moe_dispatch<ACT, TileGeo<NB>::MB_MAX>((rows + 31) >> 5, fmt, pairs, rows, topk, x, y, K,
                                                N, n0, smem, tl);
+}
+
+template <bool ACT>
+hipError_t launch_gemm(const void *x, const uint8_t *w_fp4, const uint8_t *w_scale, void *y,
+                       const MoeWs &w, int64_t P, int topk, int E, int N, int K,
+                       hipStream_t stream)
+{
+    constexpr int NB = moe_nb<ACT>();
+    constexpr int LDS = TileGeo<NB>::lds_bytes(TileGeo<NB>::MB_MAX);
+    static_assert(LDS <= 160 * 1024, "tile fits the LDS");
+    auto kern = moe_gemm_kernel<ACT>;
+    static hipError_t attr = hipErrorNotReady;
+    if (attr != hipSuccess)
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (attr != hipSuccess)
+        return attr;
+    const int tw = ACT ? moe_tn<ACT>() / 2 : moe_tn<ACT>();
+    const int nout = ACT ? N / 2 : N;
+    const int n_nt = (nout + tw - 1) / tw;
+    const int64_t grid = 8 * (((int64_t)max_tiles(P, E) * n_nt + 7) / 8);
+    if (grid > INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(TL_THREADS), (size_t)LDS, stream,
+                       static_cast<const uint16_t *>(x), w_fp4, w_scale, static_cast<uint16_t *>(y),
+                       w.hdr, w.tiles, w.sorted, topk, E, N, K, n_nt);
+    return hipGetLastError();
 }
 
 } // namespace
@@ -249,31 +290,14 @@ hipError_t launch_mxfp4_moe(const void *x, const int32_t *ids, const uint8_t *w_
     const int64_t P = (int64_t)T * topk;
     const MoeWs w = carve(workspace, P, E);
     const size_t route_lds = (size_t)(3 * (E + 1) + ROUTE_THREADS / 64) * sizeof(int);
+    const int tm = act ? moe_tm<true>() : moe_tm<false>();
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(ROUTE_THREADS), route_lds, stream, ids,
-                       (int)P, E, w.hdr, w.tiles, w.sorted);
+                       (int)P, E, tm, w.hdr, w.tiles, w.sorted);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    auto kern = act ? moe_gemm_kernel<true> : moe_gemm_kernel<false>;
-    static hipError_t attr[2] = {hipErrorNotReady, hipErrorNotReady};
-    hipError_t &ae = attr[act ? 1 : 0];
-    if (ae != hipSuccess)
-        ae = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 TileGeo<MOE_NB>::lds_bytes(TileGeo<MOE_NB>::MB_MAX));
-    if (ae != hipSuccess)
-        return ae;
-    const int tw = act ? MOE_TN / 2 : MOE_TN;
-    const int nout = act ? N / 2 : N;
-    const int n_nt = (nout + tw - 1) / tw;
-    const int64_t grid = 8 * (((int64_t)max_tiles(P, E) * n_nt + 7) / 8);
-    if (grid > INT32_MAX)
-        return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(TL_THREADS),
-                       (size_t)TileGeo<MOE_NB>::lds_bytes(TileGeo<MOE_NB>::MB_MAX), stream,
-                       static_cast<const uint16_t *>(x), w_fp4, w_scale, static_cast<uint16_t *>(y),
-                       w.hdr, w.tiles, w.sorted, topk, E, N, K, n_nt);
-    return hipGetLastError();
+    return act ? launch_gemm<true>(x, w_fp4, w_scale, y, w, P, topk, E, N, K, stream)
+               : launch_gemm<false>(x, w_fp4, w_scale, y, w, P, topk, E, N, K, stream);
 }
 
 } // namespace wob

@@ -202,27 +202,40 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
             }
         }
     }
-    // Rare large shapes: whatever did not fit the prologue registers.
-    for (int i = tid + nthr * SK_XR; i < nvec; i += nthr) {
-        const u32x4 v = xs[i];
-        float bs = 0.f;
+    // Large M * K (long rows): whatever did not fit the prologue registers,
+    // SK_XR loads per thread at a time so their latencies overlap (one load
+    // per iteration serialized a dozen L2 round trips on 1 x 21504 rows).
+    // nvec and the thread offsets of a 4-lane group are multiples of 4, so
+    // the lanes of a chunk's group enter and leave the loop together.
+    for (int i0 = tid + nthr * SK_XR; i0 < nvec; i0 += nthr * SK_XR) {
+        u32x4 v[SK_XR];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if constexpr (DT == DT_F16)
-                bs = __builtin_amdgcn_fdot2(bitcast<half2_t>(v[e]),
-                                            half2_t{(_Float16)1.f, (_Float16)1.f}, bs, false);
-            else
-                bs = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(v[e]),
-                                                     bitcast<bf162_t>(0x3F803F80u), bs, false);
+        for (int t = 0; t < SK_XR; ++t)
+            v[t] = xs[min(i0 + nthr * t, nvec - 1)];
+#pragma unroll
+        for (int t = 0; t < SK_XR; ++t) {
+            const int i = i0 + nthr * t;
+            float bs = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (DT == DT_F16)
+                    bs = __builtin_amdgcn_fdot2(bitcast<half2_t>(v[t][e]),
+                                                half2_t{(_Float16)1.f, (_Float16)1.f}, bs, false);
+                else
+                    bs = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(v[t][e]),
+                                                         bitcast<bf162_t>(0x3F803F80u), bs, false);
+            }
+            bs += __shfl_xor(bs, 1);
+            bs += __shfl_xor(bs, 2);
+            if (i < nvec) {
+                const int m = i / rowblk;
+                const int tb = i - m * rowblk;
+                const int j = tb >> 2, wi = tb & 3;
+                xl[m * RB + (j >> 3) * 32 + wi * 8 + (j & 7)] = to_word_order(v[t]);
+                if (wi == 0)
+                    xsum[m * C + j] = bs;
+            }
         }
-        bs += __shfl_xor(bs, 1);
-        bs += __shfl_xor(bs, 2);
-        const int m = i / rowblk;
-        const int tb = i - m * rowblk;
-        const int j = tb >> 2, wi = tb & 3;
-        xl[m * RB + (j >> 3) * 32 + wi * 8 + (j & 7)] = to_word_order(v);
-        if (wi == 0)
-            xsum[m * C + j] = bs;
     }
     for (int i = tid + nthr * SK_SR; i < nsb; i += nthr)
         reinterpret_cast<u32x4 *>(sl)[i] = ss[i];

@@ -88,7 +88,7 @@ constexpr int TL_ROWB = 256; // LDS bytes per activation row of a span
 // Tile geometry for NB weight blocks per wave.
 template <int NB>
 struct TileGeo {
-    static_assert(NB == 2 || NB == 4, "weight blocks per wave");
+    static_assert(NB >= 2 && NB <= 4, "weight blocks per wave");
     static constexpr int TN = 32 * NB * TL_WAVES; // weight rows per tile
     static constexpr int MB_MAX = 16 / NB;        // activation blocks per tile, at most
     static constexpr int TM_MAX = 32 * MB_MAX;
@@ -562,6 +562,7 @@ struct FmtW4 {
 // matrix row (nb % 2) * N/2 + n0 + 16 NB w + 32 (nb / 2) + i.
 template <bool PAIRED, int NB>
 struct FmtFP4 {
+    static_assert(!PAIRED || NB % 2 == 0, "gate / up blocks come in pairs");
     static constexpr int NLOADS = NB;
     struct Meta {
         uint32_t s[NB]; // E8M0 bytes of slices hf = 0 (low byte) and 1

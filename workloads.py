@@ -159,7 +159,23 @@ WORKLOADS = [
     Workload("moe_stage1", "moe", "MoE stage-1 BF16xMXFP4 1024 tokens, 32 experts, top-4, K=2880, N=5760",
              dict(T=1024, E=32, topk=4, N=5760, K=2880)),
 ]
-BY_KEY = {w.key: w for w in WORKLOADS}
+# The zero-point page's other measured shapes (its per-shape timing table and
+# its batch-4, g = 128 regression table), read as M x N x K with the shapes
+# of the batch-4 table given as N x K; fp16 like that table's "-zp" rows.
+EXTRA_WORKLOADS = [
+    Workload("decode_qkv", "w4a16", "decode skinny GEMV 1x16384x5376 g=32 fp16 (qkv shape)",
+             dict(M=1, N=16384, K=5376, g=32, dtype=F16)),
+    Workload("decode_down", "w4a16", "decode skinny GEMV 1x5376x21504 g=32 fp16 (down shape)",
+             dict(M=1, N=5376, K=21504, g=32, dtype=F16)),
+    Workload("bs4_2048x2560", "w4a16", "batch-4 skinny 4x2048x2560 g=128 fp16",
+             dict(M=4, N=2048, K=2560, g=128, dtype=F16)),
+    Workload("bs4_6144x2048", "w4a16", "batch-4 skinny 4x6144x2048 g=128 fp16",
+             dict(M=4, N=6144, K=2048, g=128, dtype=F16)),
+    Workload("bs4_4096x2048", "w4a16", "batch-4 skinny 4x4096x2048 g=128 fp16",
+             dict(M=4, N=4096, K=2048, g=128, dtype=F16)),
+]
+
+BY_KEY = {w.key: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
 
 def w4a16_bytes(M, N, K, g, act_bytes=2, symmetric=False):
