@@ -142,7 +142,8 @@ __device__ __forceinline__ void dispatch_tile(int mb, const Fmt &fmt, const Cont
 }
 
 // m_offsets == nullptr: dense problem of M rows (n_mt tiles of TM_MAX rows).
-template <int DT, int NB, bool HAS_Z>
+// GW: group size >= 64 (one scale / zero-point load per slice pair).
+template <int DT, int NB, bool HAS_Z, bool GW>
 __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros,
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
     const int n0 = nt * GEO::TN;
     const int G = K >> (5 + gshift);
     const TileLane tl;
-    const FmtW4<DT, HAS_Z, NB> fmt(qweight + (size_t)e * N * (K >> 3),
+    const FmtW4<DT, HAS_Z, NB, GW> fmt(qweight + (size_t)e * N * (K >> 3),
                                    scales + (size_t)e * N * G,
                                    HAS_Z ? qzeros + (size_t)e * (N >> 3) * G : qzeros, N, K,
                                    gshift, n0, tl);
@@ -186,12 +187,12 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
     dispatch_tile<DT, NB, GEO::MB_MAX>((rows + 31) >> 5, fmt, rws, xbase, K, N, n0, smem, tl);
 }
 
-template <int DT, int NB, bool HAS_Z>
+template <int DT, int NB, bool HAS_Z, bool GW>
 hipError_t launch_k(const W4Args &a, const int64_t *m_offsets, int num_groups, int grid, int n_mt,
                     int n_nt, size_t lds, hipStream_t stream)
 {
     const int gshift = a.g == 32 ? 0 : a.g == 64 ? 1 : 2;
-    auto kern = w4a16_tiled_kernel<DT, NB, HAS_Z>;
+    auto kern = w4a16_tiled_kernel<DT, NB, HAS_Z, GW>;
     // More than 64 KB of dynamic LDS must be requested per kernel (gfx950 has 160 KB per CU).
     static hipError_t attr = hipErrorNotReady;
     if (attr != hipSuccess)
@@ -208,8 +209,8 @@ hipError_t launch_k(const W4Args &a, const int64_t *m_offsets, int num_groups, i
     return hipGetLastError();
 }
 
-template <int DT, bool HAS_Z>
-hipError_t launch_z(const W4Args &a, const int64_t *m_offsets, int num_groups, hipStream_t stream)
+template <int DT, bool HAS_Z, bool GW>
+hipError_t launch_zg(const W4Args &a, const int64_t *m_offsets, int num_groups, hipStream_t stream)
 {
     using GEO = TileGeo<TILED_NB>;
     constexpr int TMX = GEO::TM_MAX;
@@ -219,16 +220,23 @@ hipError_t launch_z(const W4Args &a, const int64_t *m_offsets, int num_groups, h
         const int n_mt = (a.M + TMX - 1) / TMX;
         const int mb = n_mt == 1 ? (a.M + 31) / 32 : GEO::MB_MAX;
         const int grid = 8 * ((n_mt * n_nt + 7) / 8);
-        return launch_k<DT, TILED_NB, HAS_Z>(a, nullptr, 0, grid, n_mt, n_nt,
-                                             (size_t)GEO::lds_bytes(mb), stream);
+        return launch_k<DT, TILED_NB, HAS_Z, GW>(a, nullptr, 0, grid, n_mt, n_nt,
+                                                 (size_t)GEO::lds_bytes(mb), stream);
     }
     // Upper bound on the tiles of all groups: sum of ceil(rows_e / TMX).
     const int64_t max_mt = (a.M + TMX - 1) / TMX + num_groups;
     const int64_t grid = 8 * ((max_mt * n_nt + 7) / 8);
     if (grid > INT_MAX)
         return hipErrorInvalidValue;
-    return launch_k<DT, TILED_NB, HAS_Z>(a, m_offsets, num_groups, (int)grid, 0, n_nt,
-                                         (size_t)GEO::lds_bytes(GEO::MB_MAX), stream);
+    return launch_k<DT, TILED_NB, HAS_Z, GW>(a, m_offsets, num_groups, (int)grid, 0, n_nt,
+                                             (size_t)GEO::lds_bytes(GEO::MB_MAX), stream);
+}
+
+template <int DT, bool HAS_Z>
+hipError_t launch_z(const W4Args &a, const int64_t *m_offsets, int num_groups, hipStream_t stream)
+{
+    return a.g >= 64 ? launch_zg<DT, HAS_Z, true>(a, m_offsets, num_groups, stream)
+                     : launch_zg<DT, HAS_Z, false>(a, m_offsets, num_groups, stream);
 }
 
 hipError_t launch_any(const W4Args &a, const int64_t *m_offsets, int num_groups, hipStream_t stream)

@@ -485,9 +485,11 @@ __device__ __forceinline__ int xcd_tile(int tiles)
 // zero-points qzeros[N/8][K/g] (or none: z = 8).  Each lane handles rows
 // n_nb = n0 + 32 NB wave + 32 nb + nl, which share n % 8, so one nibble shift
 // of the zero-point words serves all its blocks.
-template <int DT, bool HAS_Z, int NB>
+template <int DT, bool HAS_Z, int NB, bool GW>
 struct FmtW4 {
-    static constexpr int NLOADS = NB * (HAS_Z ? 4 : 2);
+    // GW: every group spans at least 64 k (g >= 64), so a lane's two 32-wide
+    // slices of a span share one scale and one zero-point word: one load each.
+    static constexpr int NLOADS = NB * (HAS_Z ? 2 : 1) * (GW ? 1 : 2);
     struct Meta {
         uint32_t s[NB][2], z[NB][2];
     };
@@ -519,7 +521,7 @@ struct FmtW4 {
     __device__ __forceinline__ void load_meta(int span, Meta &m) const
     {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+        for (int hf = 0; hf < (GW ? 1 : 2); ++hf) {
             const int k = span * TL_SPAN + 64 * h + 32 * hf;
             const int kc = min(k, K - 32); // slice past K: clamped load, scale zeroed at use
             const uint32_t grp = (uint32_t)(kc >> (5 + gshift));
@@ -528,6 +530,13 @@ struct FmtW4 {
                 m.s[nb][hf] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + 2u * grp);
                 m.z[nb][hf] = HAS_Z ? *reinterpret_cast<const uint32_t *>(wz + zoff[nb] + 4u * grp)
                                     : 0x88888888u;
+            }
+        }
+        if constexpr (GW) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                m.s[nb][1] = m.s[nb][0]; // separate copies: the tail zeroes them per slice
+                m.z[nb][1] = m.z[nb][0];
             }
         }
     }
