@@ -18,8 +18,9 @@ launch duration and the roofline entry uses it.  The CPU baseline is the
 oracle (single-threaded C) on the full decode call.
 
 Other workloads of the pages (tiny GEMV, small batch, prefill, MoE stage 1,
-the zero-point page's qkv / down decode shapes and batch-4 g = 128 shapes) are
-measured the same way and reported under "others".
+the zero-point page's qkv / down decode shapes and batch-4 g = 128 shapes, the
+grouped GEMM on an MoE-like configuration) are measured the same way and
+reported under "others".
 """
 from __future__ import annotations
 
@@ -172,6 +173,44 @@ def bench_w4a16(wkey: str, steps: int, warmup: int):
     return res, d
 
 
+def bench_grouped(wkey: str, steps: int, warmup: int):
+    import weight_only_bit_amd as wob
+    torch = _torch()
+    w = wl.BY_KEY[wkey]
+    d = w.make(seed=0)
+    off = d["m_offsets"]
+    total_m, E, N, K, g = int(off[-1]), len(off) - 1, d["N"], d["K"], d["g"]
+    nbytes = wl.grouped_bytes(total_m, E, N, K, g)
+    flops = 2 * total_m * N * K
+    copies = _copies_for(nbytes, max_copies=4)
+    act = torch.float16 if d["dtype"] == wl.F16 else torch.bfloat16
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    bufs = [dict(x=dev(d["x"].view(np.int16)).view(act), off=dev(off), q=dev(d["qweight"]),
+                 s=dev(d["scales"].view(np.int16)).view(act), z=dev(d["qzeros"]))
+            for _ in range(copies)]
+    ys = [torch.empty((total_m, N), dtype=act, device="cuda") for _ in range(copies)]
+
+    def step(i):
+        b = bufs[i % copies]
+        wob.gemm_grouped(b["x"], b["off"], b["q"], b["s"], b["z"], g, out=ys[i % copies])
+
+    graph_ms = kern_ms = _time_steps(step, steps, warmup)
+    res = dict(workload=w.desc, groups=E, total_M=total_m, N=N, K=K, g=g,
+               dtype=wl.DTYPE_NAMES[d["dtype"]], copies=copies, bytes_per_call=nbytes,
+               flops_per_call=flops, us_per_call=round(graph_ms * 1e3, 3),
+               tflops=round(flops / (graph_ms * 1e-3) / 1e12, 2))
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    res["roofline"] = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_PEAK_TFLOPS,
+                           unit="TFLOP/s", frac=round(achieved / MFMA_PEAK_TFLOPS, 4),
+                           traffic=committed_traffic(wkey, "tiled"))
+    del bufs, ys
+    torch.cuda.empty_cache()
+    return res, d
+
+
 def bench_moe(wkey: str, steps: int, warmup: int, act: int = 0):
     import weight_only_bit_amd as wob
     torch = _torch()
@@ -295,7 +334,8 @@ def main():
             if w.key == head.key:
                 continue
             try:
-                r, _ = (bench_w4a16 if w.kind == "w4a16" else bench_moe)(w.key, args.steps, args.warmup)
+                fn = {"w4a16": bench_w4a16, "grouped": bench_grouped, "moe": bench_moe}[w.kind]
+                r, _ = fn(w.key, args.steps, args.warmup)
                 others[w.key] = r
             except Exception as e:  # report, do not hide: the entry says what failed
                 others[w.key] = dict(workload=w.desc, error=f"{type(e).__name__}: {e}")

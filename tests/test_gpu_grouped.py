@@ -72,3 +72,29 @@ def test_grouped_single_group_matches_dense(wob):
                  dev(d["qzeros"][0]), 64)
     torch.cuda.synchronize()
     assert np.array_equal(a, host_bits(y))
+
+
+def test_grouped_moe_like_full_size(wob, oracle):
+    """The MoE-like grouped configuration at full size (32 experts, 4096 routed
+    rows, N 5760, K 2880, g 32, bf16): every output finite, sampled outputs of
+    every group (its first and last row and random ones, at random columns)
+    against the oracle run on that group's rows and weights."""
+    d = wl.BY_KEY["grouped_moe_like"].make()
+    bits = _run(wob, d)
+    y = oracle.act_decode(bits, d["dtype"])
+    assert np.all(np.isfinite(y))
+    off = d["m_offsets"]
+    rng = np.random.default_rng(2)
+    for e in range(len(off) - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        rows = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 4)]))
+        ms = np.repeat(rows - lo, 16)
+        ns = rng.integers(0, d["N"], ms.size)
+        order = np.argsort(ns, kind="stable")
+        ms, ns = ms[order], ns[order]
+        yref = oracle.w4a16_gemm_sampled(d["x"][lo:hi], d["dtype"], d["qweight"][e],
+                                         d["scales"][e], d["qzeros"][e], d["K"], d["g"], ms, ns)
+        ok, err, bound = oracle.tolerance_ok(y[lo + ms, ns], yref)
+        assert ok, (e, err, bound)

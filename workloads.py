@@ -132,6 +132,20 @@ def moe_inputs(T, E, topk, N, K, seed=0, exp_lo=118, exp_hi=126):
                 w_scale=w_scale, T=T, E=E, topk=topk, N=N, K=K)
 
 
+def routed_group_rows(T, E, topk, seed=0):
+    """Rows per expert of a uniform top-k routing (the recipe of moe_inputs)."""
+    rng = np.random.default_rng(seed)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :topk]
+    return np.bincount(ids.ravel(), minlength=E).astype(np.int64)
+
+
+def grouped_bytes(total_m, E, N, K, g, act_bytes=2):
+    """Algorithmic bytes of one grouped W4A16 call: every group's packed codes,
+    scales and packed zero-points, X and Y."""
+    G = K // g
+    return E * (N * K // 2 + act_bytes * N * G + N * G // 2) + act_bytes * total_m * (K + N)
+
+
 @dataclass(frozen=True)
 class Workload:
     key: str
@@ -143,6 +157,9 @@ class Workload:
         p = dict(self.params)
         if self.kind == "w4a16":
             return w4a16_inputs(p["M"], p["N"], p["K"], p["g"], p["dtype"], seed=seed)
+        if self.kind == "grouped":
+            rows = routed_group_rows(p["T"], p["E"], p["topk"], seed=seed)
+            return w4a16_grouped_inputs(rows, p["N"], p["K"], p["g"], p["dtype"], seed=seed)
         return moe_inputs(p["T"], p["E"], p["topk"], p["N"], p["K"], seed=seed)
 
 
@@ -173,6 +190,12 @@ EXTRA_WORKLOADS = [
              dict(M=4, N=6144, K=2048, g=128, dtype=F16)),
     Workload("bs4_4096x2048", "w4a16", "batch-4 skinny 4x4096x2048 g=128 fp16",
              dict(M=4, N=4096, K=2048, g=128, dtype=F16)),
+    # The grouped GEMM on an MoE-like uint4 configuration: the MoE stage-1
+    # shape with W4A16 experts, rows per expert from a uniform top-4 routing.
+    Workload("grouped_moe_like", "grouped",
+             "grouped W4A16 32 experts x rows of 1024 tokens top-4 (4096 rows), N=5760, K=2880, "
+             "g=32 bf16",
+             dict(T=1024, E=32, topk=4, N=5760, K=2880, g=32, dtype=BF16)),
 ]
 
 BY_KEY = {w.key: w for w in WORKLOADS + EXTRA_WORKLOADS}
