@@ -217,9 +217,13 @@ def bench_moe(wkey: str, steps: int, warmup: int, act: int = 0):
     w = wl.BY_KEY[wkey]
     d = w.make(seed=0)
     T, E, topk, N, K = d["T"], d["E"], d["topk"], d["N"], d["K"]
-    nbytes = wl.moe_bytes(T, E, topk, N, K)
+    if T <= 8:  # decode batch: only the experts the ids name are streamed
+        nbytes = wl.moe_decode_bytes(d["ids"], E, N, K)
+        copies = _copies_for(nbytes, max_copies=8)
+    else:
+        nbytes = wl.moe_bytes(T, E, topk, N, K)
+        copies = _copies_for(nbytes, max_copies=4)
     flops = 2 * T * topk * N * K
-    copies = _copies_for(nbytes, max_copies=4)
 
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -243,10 +247,18 @@ def bench_moe(wkey: str, steps: int, warmup: int, act: int = 0):
                copies=copies, bytes_per_call=nbytes, flops_per_call=flops,
                us_per_call=round(graph_ms * 1e3, 3),
                tflops=round(flops / (graph_ms * 1e-3) / 1e12, 2))
-    achieved = flops / (kern_ms * 1e-3) / 1e12
-    res["roofline"] = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_PEAK_TFLOPS,
-                           unit="TFLOP/s", frac=round(achieved / MFMA_PEAK_TFLOPS, 4),
-                           traffic=committed_traffic(wkey + ("_silu" if act else ""), "moe"))
+    traffic = committed_traffic(wkey + ("_silu" if act else ""), "moe")
+    if T <= 8:  # decode batch: memory-bound, bytes of the experts the ids name
+        achieved = nbytes / (kern_ms * 1e-3) / 1e9
+        res["gbs"] = round(achieved, 1)
+        res["roofline"] = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                               unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                               traffic=traffic)
+    else:
+        achieved = flops / (kern_ms * 1e-3) / 1e12
+        res["roofline"] = dict(bound="mfma", achieved=round(achieved, 2), peak=MFMA_PEAK_TFLOPS,
+                               unit="TFLOP/s", frac=round(achieved / MFMA_PEAK_TFLOPS, 4),
+                               traffic=traffic)
     del bufs, ys
     torch.cuda.empty_cache()
     return res, d

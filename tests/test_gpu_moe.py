@@ -201,3 +201,44 @@ def test_config_moe_stage1_silu_mul_full_size(wob, oracle):
     ref = oracle.silu_mul(np.stack([gate, up], axis=-1))[..., 0]
     ok, err, bound = oracle.tolerance_ok(y[ts, ss, ns], ref)
     assert ok, (err, bound)
+
+
+# --- decode path: at most 8 tokens (split weight rows, no MFMA tiles) -------------
+
+@pytest.mark.parametrize("T,E,topk,N,K", [
+    (1, 32, 4, 5760, 2880), (8, 32, 4, 5760, 2880),  # the MoE shape with decode batches
+    (2, 8, 2, 528, 192), (3, 4, 4, 48, 64), (5, 16, 3, 272, 640),
+    (8, 64, 8, 96, 4160),    # K past 4096: four staged rows per pass, several passes per tile
+    (3, 4, 2, 64, 32768),    # one staged row per pass
+    (2, 4, 2, 32, 32832)])   # K too long to stage: the tile kernel runs instead
+def test_moe_decode_parity(wob, oracle, T, E, topk, N, K):
+    d = wl.moe_inputs(T, E, topk, N, K, seed=T * 7 + N + K)
+    _check(oracle, d, _run(wob, d))
+
+
+def test_moe_decode_invalid_and_repeated_ids(wob, oracle):
+    """Out-of-range ids write zero rows; an expert named twice by one token gets
+    two rows of the same activation."""
+    d = wl.moe_inputs(6, 8, 4, 304, 256, seed=9)
+    ids = d["ids"].copy()
+    ids[0, 0] = -1
+    ids[2, 3] = 8
+    ids[4, :] = 3  # all four slots of token 4 on expert 3
+    ids[5, 1] = ids[5, 0]
+    ybits = _run(wob, d, ids)
+    _check(oracle, d, ybits, ids)
+    assert np.all(ybits[0, 0] == 0) and np.all(ybits[2, 3] == 0)
+    assert np.array_equal(ybits[4, 0], ybits[4, 3]) and np.array_equal(ybits[5, 0], ybits[5, 1])
+
+
+@pytest.mark.parametrize("T,E,topk,N,K", [(1, 32, 4, 5760, 2880), (4, 8, 2, 32, 64),
+                                          (8, 16, 4, 576, 4160)])
+def test_moe_decode_silu_mul(wob, oracle, T, E, topk, N, K):
+    d = wl.moe_inputs(T, E, topk, N, K, seed=T + K)
+    ids = d["ids"].copy()
+    ids[0, topk - 1] = E  # out-of-range id: zero row
+    pre = oracle.mxfp4_moe_gemm(d["x"], ids, d["w_fp4"], d["w_scale"], T, topk, E, N, K)
+    ybits = _run_act(wob, d, ids)
+    ok, err, bound = oracle.tolerance_ok(oracle.bf16_decode(ybits), oracle.silu_mul(pre))
+    assert ok, f"max err {err} > bound {bound}"
+    assert np.all(ybits[0, topk - 1] == 0)

@@ -30,6 +30,8 @@
 #include "wob_internal.hpp"
 #include "wob_tile.hpp"
 
+#include <algorithm>
+
 namespace wob {
 namespace {
 
@@ -248,6 +250,280 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
                                                N, n0, smem, tl);
 }
 
+// ---- Decode path: at most MG_TOKENS tokens --------------------------------
+//
+// With a handful of tokens every expert holds one or two routed rows, so the
+// tile kernel would run a few dozen single-block workgroups, each streaming a
+// whole weight tile on its own.  This kernel splits the weight rows finely
+// instead (memory-bound, like the skinny W4A16 path): a workgroup takes one
+// expert tile and MG_WAVES x 8 weight rows; wave lane (r, q) = (lane / 8,
+// lane % 8) owns weight row r of the wave and the 16-byte code chunks
+// q, q + 8, ... of it (32 E2M1 codes and one E8M0 scale byte each).  The
+// tile's activation rows are gathered by token into LDS; each code word is
+// expanded with v_cvt_scalef32_pk_bf16_fp4 (the same conversion as the tile
+// kernel) and multiplied with v_dot2_f32_bf16 against the activation pairs
+// (exact products, fp32 accumulation).  A lane's chunks are loaded in
+// batches of MG_CB, the next batch in flight while one is computed, so the
+// whole row slice streams with about one memory latency.  With the fused
+// activation a wave's rows are 4 gate rows and the matching 4 up rows.
+constexpr int MG_TOKENS = 8;  // decode path: T <= 8
+constexpr int MG_WAVES = 4;
+constexpr int MG_THREADS = 64 * MG_WAVES;
+constexpr int MG_CB = 4;      // code chunks per lane per batch
+constexpr int MG_LDS = 64 * 1024;
+
+template <bool ACT>
+constexpr int mg_cols() { return ACT ? 4 * MG_WAVES : 8 * MG_WAVES; } // output columns per workgroup
+
+// Activation rows per pass for this K: the largest power of two <= 8 whose
+// rows fit the LDS budget (0: K too long for this path).
+int mg_rows(int K)
+{
+    int mr = 8;
+    while (mr > 0 && mr * 2 * K > MG_LDS)
+        mr >>= 1;
+    return mr;
+}
+
+// Rows 0 .. MR-1 of the staged activations times this lane's code chunks
+// j0, j0 + 8, ...  A chunk past the row has the scale byte 0 (E8M0 0 gives
+// the scale 0) and reads the row's last staged activations (finite), so it
+// adds exact zeros.
+template <int MR>
+__device__ __forceinline__ void mg_batch(const u32x4 (&w)[MG_CB], const uint32_t (&sb)[MG_CB],
+                                         const uint8_t *xl, int j0, int CK, int K2,
+                                         float (&acc)[MR])
+{
+#pragma unroll
+    for (int t = 0; t < MG_CB; ++t) {
+        const float sc = e8m0_to_f32(sb[t]);
+        u32x4 wp[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            wp[c] = fp4_word_bf16x8(w[t][c], sc); // k = 32 j + 8 c + 2 p, +1
+        const uint8_t *xc = xl + 64 * min(j0 + 8 * t, CK - 1);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const u32x4 xv = *reinterpret_cast<const u32x4 *>(xc + m * K2 + 16 * c);
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    acc[m] = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(wp[c][p]),
+                                                             bitcast<bf162_t>(xv[p]), acc[m], false);
+            }
+        }
+    }
+}
+
+// One lane's code chunks q + 8 i, i = b MG_CB .. +MG_CB-1 (clamped into the
+// row; the scale byte of a chunk past the row is 0).
+__device__ __forceinline__ void mg_load(const uint8_t *wrow, const uint8_t *srow, int CK, int q,
+                                        int nch, int b, u32x4 (&w)[MG_CB], uint32_t (&sb)[MG_CB])
+{
+#pragma unroll
+    for (int t = 0; t < MG_CB; ++t) {
+        const int i = b * MG_CB + t;
+        const int j = min(q + 8 * i, CK - 1);
+        w[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow) + j);
+        const uint32_t s = srow[j];
+        sb[t] = i < nch ? s : 0u;
+    }
+}
+
+// One pass over the staged rows 0 .. mr-1 (MR >= mr): stream the lane's
+// chunks (batch 0 already loaded into w0 / s0), reduce, store.
+template <bool ACT, int MR>
+__device__ __forceinline__ void mg_pass(const uint8_t *wrow, const uint8_t *srow, int CK, int q,
+                                        const u32x4 (&w0)[MG_CB], const uint32_t (&s0)[MG_CB],
+                                        const uint8_t *smem, int K2, const int32_t *pairs, int mr,
+                                        int col, bool cvalid, int lane, uint16_t *y, int Nout)
+{
+    const int nch = (CK - q + 7) >> 3; // chunks q + 8 i of this lane (CK >= 2)
+    const int nb = (nch + MG_CB - 1) / MG_CB;
+    float acc[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+        acc[m] = 0.f;
+    u32x4 wA[MG_CB], wB[MG_CB];
+    uint32_t sA[MG_CB], sB[MG_CB];
+#pragma unroll
+    for (int t = 0; t < MG_CB; ++t) {
+        wA[t] = w0[t];
+        sA[t] = s0[t];
+    }
+    for (int b = 0; b < nb; b += 2) {
+        if (b + 1 < nb)
+            mg_load(wrow, srow, CK, q, nch, b + 1, wB, sB);
+        mg_batch<MR>(wA, sA, smem, q + 8 * MG_CB * b, CK, K2, acc);
+        if (b + 1 < nb) {
+            if (b + 2 < nb)
+                mg_load(wrow, srow, CK, q, nch, b + 2, wA, sA);
+            mg_batch<MR>(wB, sB, smem, q + 8 * MG_CB * (b + 1), CK, K2, acc);
+        }
+    }
+    // Sum over the 8 lanes of a row; lane q = 0 holds row r's dot products.
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        float v = acc[m];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        if constexpr (ACT) {
+            const float u = __shfl_xor(v, 32); // up row r + 4 of the gate row r
+            v = v / (1.0f + expf(-v)) * u;
+        }
+        const int r = lane >> 3;
+        if ((lane & 7) == 0 && (!ACT || r < 4) && cvalid && m < mr)
+            y[(size_t)pairs[m] * Nout + col] = f32_to_act<DT_BF16>(v);
+    }
+}
+
+// Runs the pass with the smallest row count (power of two <= MR) covering mr.
+template <bool ACT, int MR>
+__device__ __forceinline__ void mg_dispatch(const uint8_t *wrow, const uint8_t *srow, int CK, int q,
+                                            const u32x4 (&w0)[MG_CB], const uint32_t (&s0)[MG_CB],
+                                            const uint8_t *smem, int K2, const int32_t *pairs,
+                                            int mr, int col, bool cvalid, int lane, uint16_t *y,
+                                            int Nout)
+{
+    if constexpr (MR > 1) {
+        if (mr <= MR / 2) {
+            mg_dispatch<ACT, MR / 2>(wrow, srow, CK, q, w0, s0, smem, K2, pairs, mr, col, cvalid,
+                                     lane, y, Nout);
+            return;
+        }
+    }
+    mg_pass<ACT, MR>(wrow, srow, CK, q, w0, s0, smem, K2, pairs, mr, col, cvalid, lane, y, Nout);
+}
+
+// Routing is folded in (no separate kernel, no workspace): workgroup
+// (slot p, slice) reads the P <= MG_PMAX ids and keeps going only when pair p
+// is the first pair of its bucket (its expert, or the bucket of ids outside
+// [0, E)); it then lists that bucket's pairs in LDS.  The order of the list
+// does not change any output value: each pair's row is computed on its own.
+// All ids are read in one round trip, and the first code batch is requested
+// as soon as the bucket is known, so the listing and the activation staging
+// overlap the weight stream instead of preceding it.
+// MR: activation rows per pass (a bucket with more pairs takes several passes).
+constexpr int MG_PMAX = MG_TOKENS * 64; // T <= 8 tokens, topk <= 64
+static_assert(MG_PMAX <= 2 * MG_THREADS, "two ids per thread");
+
+template <bool ACT, int MR>
+__global__ __launch_bounds__(MG_THREADS) void moe_gemv_kernel(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ ids,
+    const uint8_t *__restrict__ w_fp4, const uint8_t *__restrict__ w_scale,
+    uint16_t *__restrict__ y, int P, int topk, int E, int N, int K, int n_slices)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ int32_t list[MG_PMAX];
+    __shared__ int count;
+    constexpr int COLS = mg_cols<ACT>();
+    const int p = blockIdx.x / n_slices;
+    const int slice = blockIdx.x - p * n_slices;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane >> 3, q = lane & 7;
+    auto bucket = [&](int32_t id) { return (uint32_t)id < (uint32_t)E ? id : E; };
+    const int j0 = tid, j1 = tid + MG_THREADS;
+    const int e = bucket(ids[p]);
+    const int b0 = j0 < P ? bucket(ids[j0]) : -1;
+    const int b1 = j1 < P ? bucket(ids[j1]) : -1;
+    if (tid == 0)
+        count = 0;
+    if (__syncthreads_or((j0 < p && b0 == e) || (j1 < p && b1 == e)))
+        return; // an earlier workgroup slot owns this bucket
+    const int Nout = ACT ? N / 2 : N;
+    // This lane's weight row and output column (rows past the matrix are
+    // clamped and never stored).
+    int col, n;
+    if constexpr (ACT) {
+        col = slice * COLS + 4 * wave + (r & 3);
+        n = (r >> 2) * (N / 2) + min(col, N / 2 - 1);
+    } else {
+        col = slice * COLS + 8 * wave + r;
+        n = min(col, N - 1);
+    }
+    const bool cvalid = col < Nout;
+    const int CK = K >> 5;
+    const int ee = min(e, E - 1); // the invalid bucket streams nothing (loads clamped, unused)
+    const uint8_t *wrow = w_fp4 + ((size_t)ee * N + n) * (size_t)(K >> 1);
+    const uint8_t *srow = w_scale + ((size_t)ee * N + n) * (size_t)CK;
+    u32x4 w0[MG_CB];
+    uint32_t s0[MG_CB];
+    if (e < E)
+        mg_load(wrow, srow, CK, q, (CK - q + 7) >> 3, 0, w0, s0);
+    if (j0 >= p && b0 == e)
+        list[atomicAdd(&count, 1)] = j0;
+    if (j1 >= p && b1 == e)
+        list[atomicAdd(&count, 1)] = j1;
+    __syncthreads();
+    const int rows = count;
+    if (e >= E) { // ids out of range: zero rows
+        for (int idx = tid; idx < rows * COLS; idx += MG_THREADS) {
+            const int c = slice * COLS + idx % COLS;
+            if (c < Nout)
+                y[(size_t)list[idx / COLS] * Nout + c] = 0;
+        }
+        return;
+    }
+    const int K2 = 2 * K;
+    const int nv = K >> 3; // 16-byte blocks per activation row
+    for (int m0 = 0; m0 < rows; m0 += MR) {
+        const int mr = min(MR, rows - m0);
+        if (m0 > 0) {
+            __syncthreads(); // the previous pass's reads of the staged rows are done
+            mg_load(wrow, srow, CK, q, (CK - q + 7) >> 3, 0, w0, s0);
+        }
+        for (int idx = tid; idx < mr * nv; idx += MG_THREADS) {
+            const int m = idx / nv, b = idx - m * nv;
+            const int tok = list[m0 + m] / topk;
+            reinterpret_cast<u32x4 *>(smem + (size_t)m * K2)[b] =
+                reinterpret_cast<const u32x4 *>(x + (size_t)tok * K)[b];
+        }
+        __syncthreads();
+        mg_dispatch<ACT, MR>(wrow, srow, CK, q, w0, s0, smem, K2, list + m0, mr, col, cvalid,
+                             lane, y, Nout);
+    }
+}
+
+template <bool ACT, int MR>
+hipError_t launch_gemv(const void *x, const int32_t *ids, const uint8_t *w_fp4,
+                       const uint8_t *w_scale, void *y, int P, int topk, int E, int N, int K,
+                       hipStream_t stream)
+{
+    auto kern = moe_gemv_kernel<ACT, MR>;
+    static hipError_t attr = hipErrorNotReady;
+    if (attr != hipSuccess)
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, MG_LDS);
+    if (attr != hipSuccess)
+        return attr;
+    const int nout = ACT ? N / 2 : N;
+    const int n_slices = (nout + mg_cols<ACT>() - 1) / mg_cols<ACT>();
+    const int64_t grid = (int64_t)P * n_slices; // one slot per pair; non-first pairs exit
+    if (P > MG_PMAX || grid > INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(MG_THREADS), (size_t)MR * 2 * (size_t)K,
+                       stream, static_cast<const uint16_t *>(x), ids, w_fp4, w_scale,
+                       static_cast<uint16_t *>(y), P, topk, E, N, K, n_slices);
+    return hipGetLastError();
+}
+
+// Rows per pass: distinct ids per token give an expert at most T rows.
+template <bool ACT>
+hipError_t launch_gemv_t(const void *x, const int32_t *ids, const uint8_t *w_fp4,
+                         const uint8_t *w_scale, void *y, int T, int P, int topk, int E, int N,
+                         int K, int mrmax, hipStream_t stream)
+{
+    const int mr = std::min(T, mrmax);
+    if (mr > 4)
+        return launch_gemv<ACT, 8>(x, ids, w_fp4, w_scale, y, P, topk, E, N, K, stream);
+    if (mr > 2)
+        return launch_gemv<ACT, 4>(x, ids, w_fp4, w_scale, y, P, topk, E, N, K, stream);
+    if (mr > 1)
+        return launch_gemv<ACT, 2>(x, ids, w_fp4, w_scale, y, P, topk, E, N, K, stream);
+    return launch_gemv<ACT, 1>(x, ids, w_fp4, w_scale, y, P, topk, E, N, K, stream);
+}
+
 template <bool ACT>
 hipError_t launch_gemm(const void *x, const uint8_t *w_fp4, const uint8_t *w_scale, void *y,
                        const MoeWs &w, int64_t P, int topk, int E, int N, int K,
@@ -288,6 +564,12 @@ hipError_t launch_mxfp4_moe(const void *x, const int32_t *ids, const uint8_t *w_
                             int act, void *workspace, hipStream_t stream)
 {
     const int64_t P = (int64_t)T * topk;
+    const int mrmax = mg_rows(K);
+    if (T <= MG_TOKENS && mrmax > 0)
+        return act ? launch_gemv_t<true>(x, ids, w_fp4, w_scale, y, T, (int)P, topk, E, N, K,
+                                         mrmax, stream)
+                   : launch_gemv_t<false>(x, ids, w_fp4, w_scale, y, T, (int)P, topk, E, N, K,
+                                          mrmax, stream);
     const MoeWs w = carve(workspace, P, E);
     const size_t route_lds = (size_t)(3 * (E + 1) + ROUTE_THREADS / 64) * sizeof(int);
     const int tm = act ? moe_tm<true>() : moe_tm<false>();

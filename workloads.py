@@ -139,6 +139,14 @@ def routed_group_rows(T, E, topk, seed=0):
     return np.bincount(ids.ravel(), minlength=E).astype(np.int64)
 
 
+def moe_decode_bytes(ids, E, N, K):
+    """Algorithmic bytes of one MoE stage-1 call with few tokens: FP4 codes and
+    E8M0 scales of the experts the ids name (each streamed once), X, ids and Y."""
+    T, topk = ids.shape
+    used = len(np.unique(ids[(ids >= 0) & (ids < E)]))
+    return used * (N * K // 2 + N * K // 32) + 2 * T * K + 4 * T * topk + 2 * T * topk * N
+
+
 def grouped_bytes(total_m, E, N, K, g, act_bytes=2):
     """Algorithmic bytes of one grouped W4A16 call: every group's packed codes,
     scales and packed zero-points, X and Y."""
@@ -190,6 +198,10 @@ EXTRA_WORKLOADS = [
              dict(M=4, N=6144, K=2048, g=128, dtype=F16)),
     Workload("bs4_4096x2048", "w4a16", "batch-4 skinny 4x4096x2048 g=128 fp16",
              dict(M=4, N=4096, K=2048, g=128, dtype=F16)),
+    # MoE stage 1 with a decode batch: the memory-bound path.
+    Workload("moe_decode", "moe",
+             "MoE stage-1 BF16xMXFP4 decode: 4 tokens, 32 experts, top-4, K=2880, N=5760",
+             dict(T=4, E=32, topk=4, N=5760, K=2880)),
     # The grouped GEMM on an MoE-like uint4 configuration: the MoE stage-1
     # shape with W4A16 experts, rows per expert from a uniform top-4 routing.
     Workload("grouped_moe_like", "grouped",
