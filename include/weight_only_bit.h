@@ -144,6 +144,9 @@ size_t mxfp4_moe_gemm_workspace_size(int64_t T, int64_t topk, int64_t E);
  *  workspace: device memory of at least mxfp4_moe_gemm_workspace_size(T, topk, E)
  *  bytes, 16-byte aligned (else WOB_INVALID_ARG); its contents on entry do not
  *  matter.  Calls that share one workspace must be ordered on one stream.
+ *  Decode batches (T <= 8, with K <= 32768) run a memory-bound kernel that
+ *  routes on its own and leaves the workspace untouched; the workspace is
+ *  still required and checked.  Both kernels compute the same function.
  */
 int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
                    const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E, int64_t N,
