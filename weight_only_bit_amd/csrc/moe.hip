@@ -163,10 +163,10 @@ template <int MB>
 struct GatherRows {
     uint32_t xo[2 * MB];
     const int32_t *pairs; // sorted + first
-    uint16_t *y;
-    int N;
+    uint16_t *base;       // y
+    int ld;               // output row length
     __device__ __forceinline__ uint32_t off(int i) const { return xo[i]; }
-    __device__ __forceinline__ uint16_t *row(int r) const { return y + (size_t)pairs[r] * N; }
+    __device__ __forceinline__ uint32_t index(int r) const { return (uint32_t)pairs[r]; }
 };
 
 // The tile with MB 32-row blocks; ACT: the paired gate/up layout and the
@@ -179,8 +179,8 @@ __device__ __forceinline__ void moe_run(const FmtFP4<ACT, moe_nb<ACT>()> &fmt, c
 {
     GatherRows<MB> g;
     g.pairs = pairs;
-    g.y = y;
-    g.N = ACT ? N / 2 : N;
+    g.base = y;
+    g.ld = ACT ? N / 2 : N;
 #pragma unroll
     for (int i = 0; i < 2 * MB; ++i) {
         const int p = pairs[min(16 * i + tl.rl, rows - 1)];

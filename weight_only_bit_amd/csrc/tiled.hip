@@ -31,13 +31,13 @@ constexpr int TILED_NB = 2; // 32-row weight blocks per wave: 256 x 256 tiles
 // rowb (rows - 1), one add and one min per copy.
 struct ContigRows {
     int rows;
-    uint32_t o0;   // rowb * rl (this lane's first row)
-    uint32_t s16;  // rowb * 16
-    uint32_t omax; // rowb * (rows - 1)
-    uint16_t *y0;  // output row m0
-    int N;
+    uint32_t o0;    // rowb * rl (this lane's first row)
+    uint32_t s16;   // rowb * 16
+    uint32_t omax;  // rowb * (rows - 1)
+    uint16_t *base; // output row m0
+    int ld;         // N
     __device__ __forceinline__ uint32_t off(int i) const { return min(o0 + (uint32_t)i * s16, omax); }
-    __device__ __forceinline__ uint16_t *row(int r) const { return y0 + (size_t)r * N; }
+    __device__ __forceinline__ uint32_t index(int r) const { return (uint32_t)r; }
 };
 
 __device__ __forceinline__ int wave_sum_dev(int v)
@@ -181,8 +181,8 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
     rws.s16 = rowb * 16u;
     rws.omax = rowb * (uint32_t)(rows - 1);
     rws.rows = rows;
-    rws.y0 = y + (size_t)m0 * N;
-    rws.N = N;
+    rws.base = y + (size_t)m0 * N;
+    rws.ld = N;
     const uint8_t *xbase = reinterpret_cast<const uint8_t *>(x + (size_t)m0 * K);
     dispatch_tile<DT, NB, GEO::MB_MAX>((rows + 31) >> 5, fmt, rws, xbase, K, N, n0, smem, tl);
 }

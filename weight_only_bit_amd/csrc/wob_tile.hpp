@@ -99,7 +99,7 @@ struct TileGeo {
     __host__ __device__ static constexpr int lds_bytes(int mb)
     {
         const int main = 2 * 32 * mb * TL_ROWB + 2 * WBUF;
-        const int stage = 32 * mb * (2 * TN + 16);
+        const int stage = 32 * mb * (2 * TN + 16 + 4); // staged rows + row-index table
         return main > stage ? main : stage;
     }
 };
@@ -377,8 +377,20 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
 // twelfth of the prefill kernel).  Lane holds D[n = 8 g4 + 4 h + j][m = nl] of
 // block (nb, mb) in register 4 g4 + j; the tile is staged as TM rows of 256
 // activation-dtype values (row stride padded by 16 bytes against bank
-// conflicts) in the LDS the main loop has released.  `yr.row(r)` returns the
-// output row pointer of tile row r, called only for r < rows.
+// conflicts) in the LDS the main loop has released.  The output rows:
+// yr.base + yr.index(r) * yr.ld for tile row r < rows; the indices are read
+// once into LDS (for gathered MoE rows each is a global load, which the copy
+// loop would otherwise repeat for every 16-byte chunk).
+template <int DT, int MB, class YRows>
+__device__ __forceinline__ uint32_t *stage_row_index(const YRows &yr, int rows, uint8_t *tbl_lds)
+{
+    uint32_t *tbl = reinterpret_cast<uint32_t *>(tbl_lds);
+    static_assert(32 * MB <= TL_THREADS, "one row index per thread");
+    if ((int)threadIdx.x < rows)
+        tbl[threadIdx.x] = yr.index(threadIdx.x);
+    return tbl;
+}
+
 template <int DT, int NB, int MB, class YRows>
 __device__ __forceinline__ void tile_store(const float16_t (&acc)[NB][MB], const YRows &yr,
                                           int rows, int n0, int N, const TileLane &tl,
@@ -387,7 +399,8 @@ __device__ __forceinline__ void tile_store(const float16_t (&acc)[NB][MB], const
     constexpr int TN = TileGeo<NB>::TN;
     constexpr int TM = 32 * MB;
     constexpr int RS = TN * 2 + 16; // LDS bytes per staged row
-    static_assert(TM * RS <= TileGeo<NB>::lds_bytes(MB), "staging fits the tile's LDS");
+    static_assert(TM * RS + 4 * TM <= TileGeo<NB>::lds_bytes(MB), "staging fits the tile's LDS");
+    const uint32_t *tbl = stage_row_index<DT, MB>(yr, rows, smem + TM * RS);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int m = 32 * mb + tl.nl;
@@ -412,7 +425,7 @@ __device__ __forceinline__ void tile_store(const float16_t (&acc)[NB][MB], const
         const int r = i / CPR, c = i % CPR;
         const int n = n0 + 8 * c;
         if (r < rows && n < N)
-            *reinterpret_cast<u32x4 *>(yr.row(r) + n) =
+            *reinterpret_cast<u32x4 *>(yr.base + (size_t)tbl[r] * yr.ld + n) =
                 *reinterpret_cast<const u32x4 *>(smem + r * RS + 16 * c);
     }
 }
@@ -431,6 +444,7 @@ __device__ __forceinline__ void tile_store_silu_mul(const float16_t (&acc)[NB][M
     constexpr int TN = TileGeo<NB>::TN;
     constexpr int TM = 32 * MB;
     constexpr int RS = TN + 16; // LDS bytes per staged row (TN / 2 values + pad)
+    const uint32_t *tbl = stage_row_index<DT, MB>(yr, rows, smem + TM * RS);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int m = 32 * mb + tl.nl;
@@ -458,7 +472,7 @@ __device__ __forceinline__ void tile_store_silu_mul(const float16_t (&acc)[NB][M
         const int r = i / CPR, c = i % CPR;
         const int n = n0 + 8 * c;
         if (r < rows && n < I)
-            *reinterpret_cast<u32x4 *>(yr.row(r) + n) =
+            *reinterpret_cast<u32x4 *>(yr.base + (size_t)tbl[r] * yr.ld + n) =
                 *reinterpret_cast<const u32x4 *>(smem + r * RS + 16 * c);
     }
 }
