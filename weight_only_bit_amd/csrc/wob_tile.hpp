@@ -20,11 +20,11 @@
 //    accumulator blocks of 16 fp32 registers (NB * MB <= 16, so the
 //    accumulators take at most 256 of a lane's 512 registers).  TN = 128 NB.
 //    One activation operand read from LDS feeds NB MFMAs and one dequantized
-//    weight word feeds MB, so NB trades LDS reads (measured: each read the
-//    wave issues between its MFMAs stalls the matrix pipe) for dequantization
-//    work.  NB = 4, MB = 4 (512 x 128) also moves the fewest bytes into LDS
-//    per MFMA for 4-bit weights and 16-bit activations (2 TM + TN / 2 bytes
-//    per k is smallest at TN = 4 TM).
+//    weight word feeds MB, so NB trades LDS reads for dequantization work.
+//    Measured on MI355X, the dequantization weighs more: NB = 2 (256 x 256)
+//    for W4A16; NB = 3 (384 x 160) for MoE experts of ~128 rows; NB = 4
+//    (512 x 128) was slower for both, although it moves the fewest bytes into
+//    LDS per MFMA (2 TM + TN / 2 bytes per k is smallest at TN = 4 TM).
 //  * K advances in spans of 128 (8 MFMA steps of 16).  Lane (nl, h) =
 //    (lane % 32, lane / 32) takes 32 bytes of weight row nl of each block:
 //    words 8h .. 8h+7 of the span, i.e. k = 64h .. 64h+63 of the span, as two
@@ -265,6 +265,7 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
     // burst.
     constexpr int NM = NB * MB;
     constexpr int GR = NM < 4 ? NM : 4; // group g: MFMAs [g NM / GR, (g + 1) NM / GR)
+    static_assert(ND <= 8 * GR, "every copy of the next span gets a slot");
 
     // One span: MFMAs on LDS buffers span & 1 with the scales in `cur`.  At
     // entry the next span's scales (the other buffer) have landed or are in
