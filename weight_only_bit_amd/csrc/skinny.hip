@@ -27,7 +27,13 @@
 // LDS with a few coalesced 16-byte loads per thread.  Each wave issues its
 // first batch of weight loads before it waits for the staging loads, so the
 // prologue latency hides behind weight traffic.  The per-chunk metadata then
-// costs two LDS reads instead of two small global loads.
+// costs two LDS reads instead of two small global loads.  With K split over
+// the waves (few rows, long rows) the scales are not staged: each lane loads
+// its chunk's scale next to the weights, through the ring, with an ordinary
+// cached load (a non-temporal one refetched the line for every 16 bytes and
+// ran slower).  On the 1 x 5376 x 21504 shape this is what lets three
+// workgroups share a CU instead of two (LDS), so the grid of 672 workgroups
+// runs in one generation (21.1 -> 16.8 us measured).
 //
 // Arithmetic: each word is unpacked with byte permutes into four pairs of
 // biased 16-bit numbers (B + q), B = 1024 for binary16 and 128 for bfloat16,
@@ -42,7 +48,10 @@
 // its slot, which immediately receives the load of chunk i + D.  One load is
 // issued per chunk computed, so each wave's requests stay smooth instead of
 // bursty (measured: batches of several chunks per issue point run slower),
-// and D - 1 chunks per row stay in flight while a chunk is computed.
+// and D - 1 chunks per row stay in flight while a chunk is computed (D = 3;
+// 6 ran slower on the split-K shapes measured).  When fewer than D chunks remain
+// after the ring's contents, they are loaded into slots as these free up, so
+// a short row's last chunks are not fetched one round trip at a time.
 // Partial sums are reduced over the 8 lanes of a row with cross-lane moves
 // and, for ksplit > 1, over waves through LDS.
 #include "wob_device.hpp"
@@ -63,15 +72,16 @@ constexpr int SK_SR = 3; // 16-byte scale blocks
 constexpr int SK_ZR = 3; // zero-point words
 
 // LDS carve-up, in bytes, shared by the kernel and the host-side size check.
+// Scales are staged only when `sc_lds` (see the kernel's SG parameter).
 struct SkLds {
     int x, xsum, sc, zp, red, total;
-    __host__ __device__ SkLds(int M, int K, int G, int octs_per_wg)
+    __host__ __device__ SkLds(int M, int K, int G, int octs_per_wg, bool sc_lds)
     {
         const int RB = ((K + 255) >> 8) * 32; // 16-byte blocks per X row
         x = 0;
         xsum = x + M * RB * 16;
         sc = xsum + M * (K >> 5) * 4;
-        zp = sc + ((octs_per_wg * 8 * G * 2 + 15) & ~15);
+        zp = sc + (sc_lds ? ((octs_per_wg * 8 * G * 2 + 15) & ~15) : 0);
         red = zp + ((octs_per_wg * G * 4 + 15) & ~15);
         total = red + SK_MAX_WAVES * 2 * M * 8 * 4; // up to two octets per wave
     }
@@ -82,7 +92,11 @@ struct SkLds {
 template <int M, int RO>
 constexpr int sk_min_waves() { return RO == 2 ? 3 : (M <= 2 ? 4 : 2); }
 
-template <int DT, int M, int D, int GS, bool HAS_Z, int RO>
+// SG: scales are read from global memory with the weights (one 2-byte load
+// per row and chunk, through the same ring) instead of being staged in LDS.
+// Used with split K, where the staged scales would cost a resident
+// workgroup per CU on long rows.
+template <int DT, int M, int D, int GS, bool HAS_Z, int RO, bool SG>
 __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16_skinny_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros,
@@ -95,7 +109,7 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
     const int NO = N >> 3; // row octets
     const int nthr = blockDim.x; // 64 * waves of this workgroup
     const int octs_per_wg = (nthr >> 6) / ksplit * RO;
-    const SkLds L(M, K, G, octs_per_wg);
+    const SkLds L(M, K, G, octs_per_wg, !SG);
     u32x4 *xl = reinterpret_cast<u32x4 *>(smem + L.x);
     float *xsum = reinterpret_cast<float *>(smem + L.xsum);
     uint16_t *sl = reinterpret_cast<uint16_t *>(smem + L.sc);
@@ -118,9 +132,11 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
     const u32x4 *ss = reinterpret_cast<const u32x4 *>(scales + (size_t)oct0 * 8 * G);
     const int nsb = nocts * G; // 16-byte blocks of this workgroup's scales
     u32x4 sr[SK_SR];
+    if constexpr (!SG) {
 #pragma unroll
-    for (int t = 0; t < SK_SR; ++t)
-        sr[t] = ss[min(tid + nthr * t, nsb - 1)];
+        for (int t = 0; t < SK_SR; ++t)
+            sr[t] = ss[min(tid + nthr * t, nsb - 1)];
+    }
     const uint32_t *zs = HAS_Z ? qzeros + (size_t)oct0 * G : nullptr;
     const int nzw = nocts * G;
     uint32_t zr[SK_ZR];
@@ -142,20 +158,31 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
     const int jf = c0 + q; // this lane's first chunk
     const int n_it = (oct < NO && jf < c1) ? (c1 - jf + 7) >> 3 : 0;
     const int jfc = min(jf, C - 1);
-    const u32x4 *wp[RO]; // row r of each octet (clamped into the matrix)
+    const u32x4 *wp[RO];    // row r of each octet (clamped into the matrix)
+    const uint16_t *sg[RO]; // its scale of chunk jfc (SG)
 #pragma unroll
-    for (int o = 0; o < RO; ++o)
-        wp[o] = reinterpret_cast<const u32x4 *>(qweight +
-                                                (size_t)(min(oct + o, NO - 1) * 8 + r) * (K >> 3)) +
-                jfc;
+    for (int o = 0; o < RO; ++o) {
+        const size_t row = (size_t)(min(oct + o, NO - 1) * 8 + r);
+        wp[o] = reinterpret_cast<const u32x4 *>(qweight + row * (K >> 3)) + jfc;
+        sg[o] = scales + row * G + (jfc >> GS);
+    }
+    constexpr int SU = 8 >> GS; // scale / zero-point index step per chunk step of 8
 
+    // Weight (and, with SG, scale) loads of this lane's chunk i into a ring slot.
+    auto load_chunk = [&](u32x4(&w)[RO], uint32_t(&sv)[RO], int i) {
+#pragma unroll
+        for (int o = 0; o < RO; ++o) {
+            w[o] = __builtin_nontemporal_load(wp[o] + 8 * i);
+            if constexpr (SG)
+                sv[o] = sg[o][SU * i]; // cached: later chunks of the wave read the same line
+        }
+    };
     // Fill the ring with chunks 0..D-1 before any wait (clamped into the row).
     u32x4 ring[D][RO];
+    uint32_t sring[D][RO]; // raw scale bits (SG only)
 #pragma unroll
     for (int d = 0; d < D; ++d)
-#pragma unroll
-        for (int o = 0; o < RO; ++o)
-            ring[d][o] = __builtin_nontemporal_load(wp[o] + 8 * min(d, max(n_it - 1, 0)));
+        load_chunk(ring[d], sring[d], min(d, max(n_it - 1, 0)));
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- stage X (word order, conflict-free block layout) and chunk sums ----
@@ -186,12 +213,14 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
         }
     }
     {
-        u32x4 *sd = reinterpret_cast<u32x4 *>(sl);
+        if constexpr (!SG) {
+            u32x4 *sd = reinterpret_cast<u32x4 *>(sl);
 #pragma unroll
-        for (int t = 0; t < SK_SR; ++t) {
-            const int i = tid + nthr * t;
-            if (i < nsb)
-                sd[i] = sr[t];
+            for (int t = 0; t < SK_SR; ++t) {
+                const int i = tid + nthr * t;
+                if (i < nsb)
+                    sd[i] = sr[t];
+            }
         }
         if constexpr (HAS_Z) {
 #pragma unroll
@@ -237,8 +266,10 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
             }
         }
     }
-    for (int i = tid + nthr * SK_SR; i < nsb; i += nthr)
-        reinterpret_cast<u32x4 *>(sl)[i] = ss[i];
+    if constexpr (!SG) {
+        for (int i = tid + nthr * SK_SR; i < nsb; i += nthr)
+            reinterpret_cast<u32x4 *>(sl)[i] = ss[i];
+    }
     if constexpr (HAS_Z) {
         for (int i = tid + nthr * SK_ZR; i < nzw; i += nthr)
             zl[i] = zs[i];
@@ -247,7 +278,6 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
 
     constexpr uint32_t MAGIC = DT == DT_F16 ? MAGIC4_F16 : MAGIC4_BF16;
     constexpr float BIAS = DT == DT_F16 ? 1024.f : 128.f;
-    constexpr int SU = 8 >> GS; // scale / zero-point index step per chunk step of 8
 
     float acc[RO][M];
 #pragma unroll
@@ -265,14 +295,14 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
         const uint16_t *sp = sl + (woct * 8 + r) * G + (jf >> GS); // octet o: + 8 G o
         const uint32_t *zp = zl + woct * G + (jf >> GS);            // octet o: + G o
 
-        auto chunk = [&](int i, const u32x4(&wv)[RO]) {
+        auto chunk = [&](int i, const u32x4(&wv)[RO], const uint32_t(&sv)[RO]) {
             // unpack every row's word pairs first; then, per activation row,
             // read that row's X blocks once and use them for all RO rows
             u32x4 pr[RO][4];
             float sc[RO], bias[RO];
 #pragma unroll
             for (int o = 0; o < RO; ++o) {
-                sc[o] = act_to_f32<DT>(sp[8 * G * o + SU * i]);
+                sc[o] = act_to_f32<DT>(SG ? (uint16_t)sv[o] : sp[8 * G * o + SU * i]);
                 const uint32_t z = HAS_Z ? nib(zp[G * o + SU * i], r) : 8u;
                 bias[o] = BIAS + (float)z;
 #pragma unroll
@@ -317,26 +347,35 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
         for (; i + 2 * D <= n_it; i += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                chunk(i + d, ring[d]);
+                chunk(i + d, ring[d], sring[d]);
                 __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int o = 0; o < RO; ++o)
-                    ring[d][o] = __builtin_nontemporal_load(wp[o] + 8 * (i + d + D));
+                load_chunk(ring[d], sring[d], i + d + D);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // Drain: the ring holds chunks i .. i+D-1 (those below n_it); the
-        // fewer than D chunks after them are loaded one at a time.
+        // Drain: the ring holds chunks i .. i+D-1 (those below n_it) and fewer
+        // than D chunks follow them.  Those are loaded into the slots as they
+        // free up (addresses clamped to the last chunk, so the loads stay
+        // unconditional), so they too are in flight together rather than
+        // one round trip each.
+        if (__any(i + D < n_it)) {
 #pragma unroll
-        for (int d = 0; d < D; ++d)
-            if (i + d < n_it)
-                chunk(i + d, ring[d]);
-        for (int j = i + D; j < n_it; ++j) {
-            u32x4 w1[RO];
+            for (int d = 0; d < D; ++d) {
+                if (i + d < n_it)
+                    chunk(i + d, ring[d], sring[d]);
+                __builtin_amdgcn_sched_barrier(0);
+                load_chunk(ring[d], sring[d], min(i + D + d, n_it - 1));
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
-            for (int o = 0; o < RO; ++o)
-                w1[o] = __builtin_nontemporal_load(wp[o] + 8 * j);
-            chunk(j, w1);
+            for (int d = 0; d < D; ++d)
+                if (i + D + d < n_it)
+                    chunk(i + D + d, ring[d], sring[d]);
+        } else {
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+                if (i + d < n_it)
+                    chunk(i + d, ring[d], sring[d]);
         }
     }
 
@@ -435,35 +474,40 @@ SkCfg sk_config(int M, int N, int K)
 int lds_bytes(int M, int N, int K, int g)
 {
     const SkCfg c = sk_config(M, N, K);
-    return SkLds(M, K, K / g, c.waves / c.ksplit * c.ro).total;
+    return SkLds(M, K, K / g, c.waves / c.ksplit * c.ro, c.ksplit == 1).total;
 }
 
-template <int DT, int M, int GS, int RO>
+template <int DT, int M, int GS, int RO, int D, bool SG>
 hipError_t launch_r(const W4Args &a, const SkCfg &c, size_t lds, hipStream_t stream)
 {
     const int octs_per_wg = c.waves / c.ksplit * RO;
     const int grid = (a.N / 8 + octs_per_wg - 1) / octs_per_wg;
     if (a.qzeros)
-        hipLaunchKernelGGL((w4a16_skinny_kernel<DT, M, SK_RING, GS, true, RO>), dim3(grid),
+        hipLaunchKernelGGL((w4a16_skinny_kernel<DT, M, D, GS, true, RO, SG>), dim3(grid),
                            dim3(64 * c.waves), lds, stream, static_cast<const uint16_t *>(a.x),
                            a.qweight, static_cast<const uint16_t *>(a.scales), a.qzeros,
                            static_cast<uint16_t *>(a.y), a.N, a.K, c.ksplit);
     else
-        hipLaunchKernelGGL((w4a16_skinny_kernel<DT, M, SK_RING, GS, false, RO>), dim3(grid),
+        hipLaunchKernelGGL((w4a16_skinny_kernel<DT, M, D, GS, false, RO, SG>), dim3(grid),
                            dim3(64 * c.waves), lds, stream, static_cast<const uint16_t *>(a.x),
                            a.qweight, static_cast<const uint16_t *>(a.scales), a.qzeros,
                            static_cast<uint16_t *>(a.y), a.N, a.K, c.ksplit);
     return hipGetLastError();
 }
 
+// Split K: scales from global memory (on the 1 x 5376 x 21504 down shape this
+// lets three workgroups share a CU instead of two, so the grid runs in one
+// generation).  Otherwise: scales staged in LDS.
 template <int DT, int M, int GS>
 hipError_t launch_g(const W4Args &a, const SkCfg &c, size_t lds, hipStream_t stream)
 {
+    if (c.ksplit > 1)
+        return launch_r<DT, M, GS, 1, SK_RING, true>(a, c, lds, stream);
     if constexpr (M <= 2) {
         if (c.ro == 2)
-            return launch_r<DT, M, GS, 2>(a, c, lds, stream);
+            return launch_r<DT, M, GS, 2, SK_RING, false>(a, c, lds, stream);
     }
-    return launch_r<DT, M, GS, 1>(a, c, lds, stream);
+    return launch_r<DT, M, GS, 1, SK_RING, false>(a, c, lds, stream);
 }
 
 template <int DT, int M>
