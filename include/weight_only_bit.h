@@ -34,9 +34,12 @@
  *
  * Conventions shared by every entry point:
  *  - All pointers are owned by the caller; the library keeps no allocation and
- *    no state beyond a per-device architecture check.
+ *    no state beyond a per-device architecture check and the per-device LDS
+ *    limit of its large-tile kernels (set on first use).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
- *    void*, NULL = the null stream); nothing synchronizes.
+ *    void*, NULL = the null stream) for the calling thread's current HIP
+ *    device, which the stream and every pointer must belong to; nothing
+ *    synchronizes.
  *  - Every argument is validated before any device call; on a non-zero status
  *    nothing was enqueued.  No exception crosses the ABI.
  *  - Device pointers must be 16-byte aligned.

@@ -31,8 +31,9 @@ int ok()
     return WOB_OK;
 }
 
-// Per-device cache of the architecture check: 0 unknown, 1 gfx950, 2 other.
-int g_arch[64];
+// Per-device cache of the architecture check: 0 unknown, 1 gfx950, 2 other
+// (atomic: calls may come from several host threads).
+std::atomic<int> g_arch[64];
 
 int arch_gate()
 {
@@ -42,14 +43,16 @@ int arch_gate()
         return fail(WOB_HIP, "hipGetDevice: %s", hipGetErrorString(e));
     if (dev < 0 || dev >= 64)
         return fail(WOB_UNSUPPORTED, "device ordinal %d out of range", dev);
-    if (g_arch[dev] == 0) {
+    int arch = g_arch[dev].load(std::memory_order_relaxed);
+    if (arch == 0) {
         hipDeviceProp_t prop;
         e = hipGetDeviceProperties(&prop, dev);
         if (e != hipSuccess)
             return fail(WOB_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
-        g_arch[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        arch = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch[dev].store(arch, std::memory_order_relaxed);
     }
-    if (g_arch[dev] != 1)
+    if (arch != 1)
         return fail(WOB_UNSUPPORTED, "device %d is not gfx950", dev);
     return WOB_OK;
 }

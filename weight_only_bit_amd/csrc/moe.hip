@@ -491,12 +491,10 @@ hipError_t launch_gemv(const void *x, const int32_t *ids, const uint8_t *w_fp4,
                        hipStream_t stream)
 {
     auto kern = moe_gemv_kernel<ACT, MR>;
-    static hipError_t attr = hipErrorNotReady;
-    if (attr != hipSuccess)
-        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, MG_LDS);
-    if (attr != hipSuccess)
-        return attr;
+    static std::atomic<uint64_t> lds_set{0};
+    if (const hipError_t e = lds_optin(reinterpret_cast<const void *>(kern), MG_LDS, lds_set);
+        e != hipSuccess)
+        return e;
     const int nout = ACT ? N / 2 : N;
     const int n_slices = (nout + mg_cols<ACT>() - 1) / mg_cols<ACT>();
     const int64_t grid = (int64_t)P * n_slices; // one slot per pair; non-first pairs exit
@@ -533,12 +531,10 @@ hipError_t launch_gemm(const void *x, const uint8_t *w_fp4, const uint8_t *w_sca
     constexpr int LDS = TileGeo<NB>::lds_bytes(TileGeo<NB>::MB_MAX);
     static_assert(LDS <= 160 * 1024, "tile fits the LDS");
     auto kern = moe_gemm_kernel<ACT>;
-    static hipError_t attr = hipErrorNotReady;
-    if (attr != hipSuccess)
-        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-    if (attr != hipSuccess)
-        return attr;
+    static std::atomic<uint64_t> lds_set{0};
+    if (const hipError_t e = lds_optin(reinterpret_cast<const void *>(kern), LDS, lds_set);
+        e != hipSuccess)
+        return e;
     const int tw = ACT ? moe_tn<ACT>() / 2 : moe_tn<ACT>();
     const int nout = ACT ? N / 2 : N;
     const int n_nt = (nout + tw - 1) / tw;

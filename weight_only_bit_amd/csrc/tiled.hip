@@ -193,14 +193,11 @@ hipError_t launch_k(const W4Args &a, const int64_t *m_offsets, int num_groups, i
 {
     const int gshift = a.g == 32 ? 0 : a.g == 64 ? 1 : 2;
     auto kern = w4a16_tiled_kernel<DT, NB, HAS_Z, GW>;
-    // More than 64 KB of dynamic LDS must be requested per kernel (gfx950 has 160 KB per CU).
-    static hipError_t attr = hipErrorNotReady;
-    if (attr != hipSuccess)
-        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize,
-                                   TileGeo<NB>::lds_bytes(TileGeo<NB>::MB_MAX));
-    if (attr != hipSuccess)
-        return attr;
+    static std::atomic<uint64_t> lds_set{0};
+    if (const hipError_t e = lds_optin(reinterpret_cast<const void *>(kern),
+                                       TileGeo<NB>::lds_bytes(TileGeo<NB>::MB_MAX), lds_set);
+        e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(TL_THREADS), lds, stream,
                        static_cast<const uint16_t *>(a.x), a.qweight,
                        static_cast<const uint16_t *>(a.scales), a.qzeros,

@@ -5,7 +5,28 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace wob {
+
+// A kernel that uses more than 64 KB of dynamic LDS (gfx950 has 160 KB per
+// CU) must raise its limit with hipFuncSetAttribute, once for every device it
+// runs on (the attribute belongs to the device's context).  `done` holds one
+// bit per device ordinal already set; the caller keeps one per kernel.
+inline hipError_t lds_optin(const void *kern, int bytes, std::atomic<uint64_t> &done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit))
+        return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit)
+        done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 struct W4Args {
     const void *x;
