@@ -262,14 +262,17 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
 // tile's activation rows are gathered by token into LDS; each code word is
 // expanded with v_cvt_scalef32_pk_bf16_fp4 (the same conversion as the tile
 // kernel) and multiplied with v_dot2_f32_bf16 against the activation pairs
-// (exact products, fp32 accumulation).  A lane's chunks are loaded in
-// batches of MG_CB, the next batch in flight while one is computed, so the
-// whole row slice streams with about one memory latency.  With the fused
-// activation a wave's rows are 4 gate rows and the matching 4 up rows.
+// (exact products, fp32 accumulation).  A lane's chunks stream through a
+// ring of MG_D slots that is filled as soon as the expert is known: a
+// 2880-long row gives a lane at most 12 chunks, so its whole slice is in
+// flight at once, behind the listing and the activation staging, and the
+// workgroup waits for memory about twice (ids, then weights) instead of once
+// per batch.  With the fused activation a wave's rows are 4 gate rows and
+// the matching 4 up rows.
 constexpr int MG_TOKENS = 8;  // decode path: T <= 8
 constexpr int MG_WAVES = 4;
 constexpr int MG_THREADS = 64 * MG_WAVES;
-constexpr int MG_CB = 4;      // code chunks per lane per batch
+constexpr int MG_D = 12;      // chunk slots per lane in the load ring
 constexpr int MG_LDS = 64 * 1024;
 
 template <bool ACT>
@@ -285,82 +288,93 @@ int mg_rows(int K)
     return mr;
 }
 
-// Rows 0 .. MR-1 of the staged activations times this lane's code chunks
-// j0, j0 + 8, ...  A chunk past the row has the scale byte 0 (E8M0 0 gives
-// the scale 0) and reads the row's last staged activations (finite), so it
-// adds exact zeros.
-template <int MR>
-__device__ __forceinline__ void mg_batch(const u32x4 (&w)[MG_CB], const uint32_t (&sb)[MG_CB],
-                                         const uint8_t *xl, int j0, int CK, int K2,
-                                         float (&acc)[MR])
-{
-#pragma unroll
-    for (int t = 0; t < MG_CB; ++t) {
-        const float sc = e8m0_to_f32(sb[t]);
-        u32x4 wp[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            wp[c] = fp4_word_bf16x8(w[t][c], sc); // k = 32 j + 8 c + 2 p, +1
-        const uint8_t *xc = xl + 64 * min(j0 + 8 * t, CK - 1);
-#pragma unroll
-        for (int m = 0; m < MR; ++m) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u32x4 xv = *reinterpret_cast<const u32x4 *>(xc + m * K2 + 16 * c);
-#pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    acc[m] = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(wp[c][p]),
-                                                             bitcast<bf162_t>(xv[p]), acc[m], false);
-            }
-        }
+// A lane's code chunk i (chunk q + 8 i of its row, clamped into the row) and
+// its E8M0 scale byte.
+struct MgRow {
+    const uint8_t *w, *s; // the row's codes and scale bytes
+    int CK, q;            // chunks per row, this lane's first chunk
+    __device__ __forceinline__ void load(int i, u32x4 &wv, uint32_t &sb) const
+    {
+        int j = min(q + 8 * i, CK - 1);
+        // opaque to the optimizer: otherwise every ring slot keeps its own
+        // pair of 64-bit address registers (one strength-reduced pointer per
+        // slot), which costs more registers than the slots themselves
+        asm volatile("" : "+v"(j));
+        wv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w) + j);
+        sb = s[j];
     }
-}
+};
 
-// One lane's code chunks q + 8 i, i = b MG_CB .. +MG_CB-1 (clamped into the
-// row; the scale byte of a chunk past the row is 0).
-__device__ __forceinline__ void mg_load(const uint8_t *wrow, const uint8_t *srow, int CK, int q,
-                                        int nch, int b, u32x4 (&w)[MG_CB], uint32_t (&sb)[MG_CB])
+// Chunk j of the row times rows 0 .. mr-1 of the staged activations (mr <= MR;
+// rows past mr are skipped by a uniform branch).
+template <int MR>
+__device__ __forceinline__ void mg_chunk(const u32x4 &w, uint32_t sb, const uint8_t *xl, int j,
+                                         int K2, int mr, float (&acc)[MR])
 {
+    const float sc = e8m0_to_f32(sb);
+    u32x4 wp[4];
 #pragma unroll
-    for (int t = 0; t < MG_CB; ++t) {
-        const int i = b * MG_CB + t;
-        const int j = min(q + 8 * i, CK - 1);
-        w[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow) + j);
-        const uint32_t s = srow[j];
-        sb[t] = i < nch ? s : 0u;
+    for (int c = 0; c < 4; ++c)
+        wp[c] = fp4_word_bf16x8(w[c], sc); // k = 32 j + 8 c + 2 p, +1
+    const uint8_t *xc = xl + 64 * j;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        if (m >= mr)
+            break;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 xv = *reinterpret_cast<const u32x4 *>(xc + m * K2 + 16 * c);
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                acc[m] = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(wp[c][p]),
+                                                         bitcast<bf162_t>(xv[p]), acc[m], false);
+        }
     }
 }
 
 // One pass over the staged rows 0 .. mr-1 (MR >= mr): stream the lane's
-// chunks (batch 0 already loaded into w0 / s0), reduce, store.
+// chunks (the ring holds chunks 0 .. MG_D-1 on entry), reduce, store.
 template <bool ACT, int MR>
-__device__ __forceinline__ void mg_pass(const uint8_t *wrow, const uint8_t *srow, int CK, int q,
-                                        const u32x4 (&w0)[MG_CB], const uint32_t (&s0)[MG_CB],
-                                        const uint8_t *smem, int K2, const int32_t *pairs, int mr,
-                                        int col, bool cvalid, int lane, uint16_t *y, int Nout)
+__device__ __forceinline__ void mg_pass(const MgRow &wr, u32x4 (&rw)[MG_D],
+                                        uint32_t (&rs)[MG_D], const uint8_t *smem, int K2,
+                                        const int32_t *pairs, int mr, int col, bool cvalid,
+                                        int lane, uint16_t *y, int Nout)
 {
-    const int nch = (CK - q + 7) >> 3; // chunks q + 8 i of this lane (CK >= 2)
-    const int nb = (nch + MG_CB - 1) / MG_CB;
+    const int nch = (wr.CK - wr.q + 7) >> 3; // chunks q + 8 i of this lane (CK >= 2)
     float acc[MR];
 #pragma unroll
     for (int m = 0; m < MR; ++m)
         acc[m] = 0.f;
-    u32x4 wA[MG_CB], wB[MG_CB];
-    uint32_t sA[MG_CB], sB[MG_CB];
+    // Steady state (rows longer than the ring): compute chunk i + d from
+    // slot d, then refill the slot with chunk i + d + MG_D.
+    int i = 0;
+    for (; i + 2 * MG_D <= nch; i += MG_D) {
 #pragma unroll
-    for (int t = 0; t < MG_CB; ++t) {
-        wA[t] = w0[t];
-        sA[t] = s0[t];
-    }
-    for (int b = 0; b < nb; b += 2) {
-        if (b + 1 < nb)
-            mg_load(wrow, srow, CK, q, nch, b + 1, wB, sB);
-        mg_batch<MR>(wA, sA, smem, q + 8 * MG_CB * b, CK, K2, acc);
-        if (b + 1 < nb) {
-            if (b + 2 < nb)
-                mg_load(wrow, srow, CK, q, nch, b + 2, wA, sA);
-            mg_batch<MR>(wB, sB, smem, q + 8 * MG_CB * (b + 1), CK, K2, acc);
+        for (int d = 0; d < MG_D; ++d) {
+            mg_chunk<MR>(rw[d], rs[d], smem, wr.q + 8 * (i + d), K2, mr, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            wr.load(i + d + MG_D, rw[d], rs[d]);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    }
+    // Drain: the ring holds chunks i .. i + MG_D - 1 (those below nch);
+    // fewer than MG_D follow, loaded into the slots as these free up.
+    if (__any(i + MG_D < nch)) {
+#pragma unroll
+        for (int d = 0; d < MG_D; ++d) {
+            if (i + d < nch)
+                mg_chunk<MR>(rw[d], rs[d], smem, wr.q + 8 * (i + d), K2, mr, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            wr.load(min(i + MG_D + d, max(nch - 1, 0)), rw[d], rs[d]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        i += MG_D;
+    }
+#pragma unroll
+    for (int d = 0; d < MG_D; ++d) {
+        if (i + d < nch)
+            mg_chunk<MR>(rw[d], rs[d], smem, wr.q + 8 * (i + d), K2, mr, acc);
+        __builtin_amdgcn_sched_barrier(0); // one chunk's unpacked words live at a time
     }
     // Sum over the 8 lanes of a row; lane q = 0 holds row r's dot products.
 #pragma unroll
@@ -377,24 +391,6 @@ __device__ __forceinline__ void mg_pass(const uint8_t *wrow, const uint8_t *srow
         if ((lane & 7) == 0 && (!ACT || r < 4) && cvalid && m < mr)
             y[(size_t)pairs[m] * Nout + col] = f32_to_act<DT_BF16>(v);
     }
-}
-
-// Runs the pass with the smallest row count (power of two <= MR) covering mr.
-template <bool ACT, int MR>
-__device__ __forceinline__ void mg_dispatch(const uint8_t *wrow, const uint8_t *srow, int CK, int q,
-                                            const u32x4 (&w0)[MG_CB], const uint32_t (&s0)[MG_CB],
-                                            const uint8_t *smem, int K2, const int32_t *pairs,
-                                            int mr, int col, bool cvalid, int lane, uint16_t *y,
-                                            int Nout)
-{
-    if constexpr (MR > 1) {
-        if (mr <= MR / 2) {
-            mg_dispatch<ACT, MR / 2>(wrow, srow, CK, q, w0, s0, smem, K2, pairs, mr, col, cvalid,
-                                     lane, y, Nout);
-            return;
-        }
-    }
-    mg_pass<ACT, MR>(wrow, srow, CK, q, w0, s0, smem, K2, pairs, mr, col, cvalid, lane, y, Nout);
 }
 
 // Routing is folded in (no separate kernel, no workspace): workgroup
@@ -445,12 +441,22 @@ __global__ __launch_bounds__(MG_THREADS) void moe_gemv_kernel(
     const bool cvalid = col < Nout;
     const int CK = K >> 5;
     const int ee = min(e, E - 1); // the invalid bucket streams nothing (loads clamped, unused)
-    const uint8_t *wrow = w_fp4 + ((size_t)ee * N + n) * (size_t)(K >> 1);
-    const uint8_t *srow = w_scale + ((size_t)ee * N + n) * (size_t)CK;
-    u32x4 w0[MG_CB];
-    uint32_t s0[MG_CB];
+    MgRow wr;
+    wr.w = w_fp4 + ((size_t)ee * N + n) * (size_t)(K >> 1);
+    wr.s = w_scale + ((size_t)ee * N + n) * (size_t)CK;
+    wr.CK = CK;
+    wr.q = q;
+    u32x4 rw[MG_D];
+    uint32_t rs[MG_D];
+    auto fill = [&]() {
+        // this lane's last chunk (a lane with no chunk, K < 256, loads chunk 0 unused)
+        const int last = max(((CK - q + 7) >> 3) - 1, 0);
+#pragma unroll
+        for (int d = 0; d < MG_D; ++d)
+            wr.load(min(d, last), rw[d], rs[d]);
+    };
     if (e < E)
-        mg_load(wrow, srow, CK, q, (CK - q + 7) >> 3, 0, w0, s0);
+        fill();
     if (j0 >= p && b0 == e)
         list[atomicAdd(&count, 1)] = j0;
     if (j1 >= p && b1 == e)
@@ -471,7 +477,7 @@ __global__ __launch_bounds__(MG_THREADS) void moe_gemv_kernel(
         const int mr = min(MR, rows - m0);
         if (m0 > 0) {
             __syncthreads(); // the previous pass's reads of the staged rows are done
-            mg_load(wrow, srow, CK, q, (CK - q + 7) >> 3, 0, w0, s0);
+            fill();
         }
         for (int idx = tid; idx < mr * nv; idx += MG_THREADS) {
             const int m = idx / nv, b = idx - m * nv;
@@ -480,8 +486,7 @@ __global__ __launch_bounds__(MG_THREADS) void moe_gemv_kernel(
                 reinterpret_cast<const u32x4 *>(x + (size_t)tok * K)[b];
         }
         __syncthreads();
-        mg_dispatch<ACT, MR>(wrow, srow, CK, q, w0, s0, smem, K2, list + m0, mr, col, cvalid,
-                             lane, y, Nout);
+        mg_pass<ACT, MR>(wr, rw, rs, smem, K2, list + m0, mr, col, cvalid, lane, y, Nout);
     }
 }
 
