@@ -17,6 +17,12 @@ graph the kernels run back to back, so the step time is the kernel's average
 launch duration and the roofline entry uses it.  The CPU baseline is the
 oracle (single-threaded C) on the full decode call.
 
+Beside each workload, `ceilings` gives references measured the same way in
+the same run: for memory-bound calls a plain streaming read of the same byte
+count (what a kernel that only reads achieves on this device), and for the
+W4A16 shapes the same product through the vendor library with 16-bit
+weights (torch.mm); for MoE stage 1 a dense bf16 GEMM of the same FLOPs.
+
 Other workloads of the pages (tiny GEMV, small batch, prefill, MoE stage 1,
 the zero-point page's qkv / down decode shapes and batch-4 g = 128 shapes, the
 grouped GEMM on an MoE-like configuration) are measured the same way and
@@ -134,6 +140,61 @@ def _time_steps(step, steps: int, warmup: int):
     return ms
 
 
+def stream_read_ceiling(nbytes: int, steps: int, warmup: int):
+    """The device's streaming-read reference for this byte count: the
+    library's plain read kernel over the same number of bytes, rotated over
+    copies like the operands (HBM, not cache), timed the same way."""
+    import weight_only_bit_amd as wob
+    torch = _torch()
+    nb = (nbytes + 15) // 16 * 16
+    copies = _copies_for(nb)
+    pool = torch.empty(copies * nb, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    views = [pool[i * nb:(i + 1) * nb] for i in range(copies)]
+
+    def step(i):
+        wob.stream_read(views[i % copies], nb, sink)
+
+    ms = _time_steps(step, steps, warmup)
+    del pool, views
+    torch.cuda.empty_cache()
+    return dict(what=f"plain streaming read of {nb:,} bytes", us=round(ms * 1e3, 3),
+                gbs=round(nb / (ms * 1e-3) / 1e9, 1))
+
+
+def library_gemm(M: int, N: int, K: int, act, steps: int, warmup: int, what: str):
+    """The same product through the vendor library (torch.mm -> hipBLASLt /
+    rocBLAS) with 16-bit weights: y[M][N] = x[M][K] w[N][K]^T, rotated over
+    weight copies like the operands."""
+    torch = _torch()
+    wbytes = N * K * 2
+    copies = _copies_for(wbytes, max_copies=64)
+    ws = [torch.empty((N, K), dtype=act, device="cuda").normal_() for _ in range(copies)]
+    x = torch.empty((M, K), dtype=act, device="cuda").normal_()
+    y = torch.empty((M, N), dtype=act, device="cuda")
+
+    def step(i):
+        torch.mm(x, ws[i % copies].t(), out=y)
+
+    ms = _time_steps(step, steps, warmup)
+    del ws, x, y
+    torch.cuda.empty_cache()
+    nbytes = wbytes + 2 * M * K + 2 * M * N
+    return dict(what=what, us=round(ms * 1e3, 3), gbs=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                tflops=round(2 * M * N * K / (ms * 1e-3) / 1e12, 2))
+
+
+def _ceilings(entries):
+    """Run each reference; a failure is reported in its entry, not raised."""
+    out = {}
+    for name, fn in entries:
+        try:
+            out[name] = fn()
+        except Exception as e:  # noqa: BLE001 - reported in the JSON line
+            out[name] = dict(error=f"{type(e).__name__}: {e}")
+    return out
+
+
 def bench_w4a16(wkey: str, steps: int, warmup: int):
     import weight_only_bit_amd as wob
     torch = _torch()
@@ -170,6 +231,13 @@ def bench_w4a16(wkey: str, steps: int, warmup: int):
                                traffic=committed_traffic(wkey, "tiled"))
     del bufs, ys
     torch.cuda.empty_cache()
+    act_name = wl.DTYPE_NAMES[d["dtype"]]
+    refs = [("library_16bit", lambda: library_gemm(
+        M, N, K, act, steps, warmup,
+        f"torch.mm {M}x{N}x{K} {act_name} with 16-bit weights ({N * K * 2:,} weight bytes)"))]
+    if skinny:
+        refs.insert(0, ("stream_read", lambda: stream_read_ceiling(nbytes, steps, warmup)))
+    res["ceilings"] = _ceilings(refs)
     return res, d
 
 
@@ -261,6 +329,15 @@ def bench_moe(wkey: str, steps: int, warmup: int, act: int = 0):
                                traffic=traffic)
     del bufs, ys
     torch.cuda.empty_cache()
+    if T <= 8:
+        res["ceilings"] = _ceilings([("stream_read",
+                                      lambda: stream_read_ceiling(nbytes, steps, warmup))])
+    elif not act:
+        P = T * topk
+        res["ceilings"] = _ceilings([("library_dense_bf16", lambda: library_gemm(
+            P, N, K, torch.bfloat16, steps, warmup,
+            f"torch.mm {P}x{N}x{K} bf16: the same FLOPs as one dense GEMM (one weight "
+            "matrix, no routing, no dequantization)"))])
     return res, d
 
 
@@ -335,6 +412,7 @@ def main():
                     flops_per_call=res["flops_per_call"]),
         us_per_call=res["us_per_call"],
         roofline=res["roofline"],
+        ceilings=res.get("ceilings"),
     )
     if not args.no_cpu_baseline and head.key == "decode_gemv":
         line["cpu_baseline"] = cpu_baseline_decode(d)

@@ -190,6 +190,17 @@ int w4a16_dequant(const int32_t *qweight, const void *scales, int scales_dtype,
 int mxfp4_dequant(const uint8_t *w_fp4, const uint8_t *w_scale, void *out, int64_t N, int64_t K,
                   void *stream);
 
+/*
+ * Streaming-read reference (a measurement aid, not part of the method): reads
+ * the `bytes` bytes at `buf` once with 16-byte loads, as fast as a kernel that
+ * only reads can, so that the GEMV kernels' rates can be compared with the
+ * device's own streaming rate for the same byte count.  bytes % 16 == 0;
+ * `buf` 16-byte aligned; `sink` is device memory of at least 1024 bytes that
+ * the call may overwrite (its contents carry no meaning).  bytes == 0 is a
+ * no-op.  Errors as for the entry points above.
+ */
+int wob_stream_read(const void *buf, size_t bytes, void *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -128,6 +128,15 @@ def test_probe_checks(L):
     assert L.lib().mxfp4_dequant(p, p, p, 8, 48, None) == L.INVALID_ARG
 
 
+def test_stream_read_checks(L):
+    f = _Fake()
+    p = f.p
+    assert L.lib().wob_stream_read(p, 24, p, None) == L.INVALID_ARG   # not a multiple of 16
+    assert L.lib().wob_stream_read(None, 32, p, None) == L.INVALID_ARG
+    assert L.lib().wob_stream_read(p, 32, None, None) == L.INVALID_ARG
+    assert L.lib().wob_stream_read(p, 0, None, None) == L.OK           # nothing to read
+
+
 def test_no_gpu_means_an_error_not_a_fallback(L):
     import torch
     if torch.cuda.is_available():

@@ -193,3 +193,15 @@ def test_mxfp4_dequant_probe_bit_exact(wob, oracle):
     out = wob.mxfp4_dequant(dev(w_fp4), dev(w_scale))
     got = oracle.bf16_decode(host_bits(out))
     assert np.array_equal(got, ref), (got[0, :16], ref[0, :16])
+
+
+def test_stream_read_reference_runs(wob):
+    """The streaming-read measurement aid reads a buffer and returns OK; its
+    sink is scratch (it holds no result to check)."""
+    torch = torch_mod()
+    buf = torch.ones(1 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    wob.stream_read(buf, buf.numel(), sink)
+    wob.stream_read(buf, 4096 + 16, sink)  # a tail shorter than one grid step
+    torch.cuda.synchronize()
+    assert torch.all(buf == 1)

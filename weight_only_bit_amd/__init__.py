@@ -22,7 +22,7 @@ from ._lib import (ACT_NONE, ACT_SILU_MUL, BF16, DTYPE, F16, F32, INVALID_ARG, O
 
 __all__ = [
     "gemm", "gemm_grouped", "mxfp4_moe_gemm", "moe_workspace_size", "w4a16_dequant",
-    "mxfp4_dequant", "device_check", "WobError", "WobDtypeError", "WobArgError",
+    "mxfp4_dequant", "stream_read", "device_check", "WobError", "WobDtypeError", "WobArgError",
     "PATH_AUTO", "PATH_SKINNY", "PATH_TILED", "ACT_NONE", "ACT_SILU_MUL",
 ]
 
@@ -168,3 +168,15 @@ def mxfp4_dequant(w_fp4, w_scale):
         st = _lib.lib().mxfp4_dequant(_ptr(w_fp4), _ptr(w_scale), _ptr(out), N, K, _stream(dev))
     _lib.check(st, "mxfp4_dequant")
     return out
+
+
+def stream_read(buf, nbytes: int, sink) -> None:
+    """Measurement aid: read nbytes of the device tensor buf once (the device's
+    streaming-read reference for a byte count); sink: >= 1024 bytes of scratch."""
+    torch = _torch()
+    dev = _check_device(buf, sink)
+    if nbytes > buf.numel() * buf.element_size() or sink.numel() * sink.element_size() < 1024:
+        raise ValueError("buffer smaller than nbytes or sink under 1024 bytes")
+    with torch.cuda.device(dev):
+        st = _lib.lib().wob_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(dev))
+    _lib.check(st, "wob_stream_read")

@@ -21,7 +21,7 @@ EXPORTS = [
     "wob_status_str", "wob_last_error", "wob_device_check",
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_grouped",
     "mxfp4_moe_gemm_workspace_size", "mxfp4_moe_gemm", "mxfp4_moe_gemm_act",
-    "w4a16_dequant", "mxfp4_dequant",
+    "w4a16_dequant", "mxfp4_dequant", "wob_stream_read",
 ]
 
 _vp = ctypes.c_void_p
@@ -43,6 +43,7 @@ _SIGNATURES = {
                                 _vp]),
     "w4a16_dequant": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _i64, _i64, _i64, _vp]),
     "mxfp4_dequant": (_i, [_vp, _vp, _vp, _i64, _i64, _vp]),
+    "wob_stream_read": (_i, [_vp, _sz, _vp, _vp]),
 }
 
 _lib = None

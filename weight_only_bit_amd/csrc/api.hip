@@ -301,4 +301,22 @@ int mxfp4_dequant(const uint8_t *w_fp4, const uint8_t *w_scale, void *out, int64
                     "mxfp4 dequant probe");
 }
 
+int wob_stream_read(const void *buf, size_t bytes, void *sink, void *stream)
+{
+    if (bytes % 16 != 0)
+        return fail(WOB_INVALID_ARG, "bytes %zu is not a multiple of 16", bytes);
+    if (bytes == 0)
+        return ok();
+    if (!buf || !sink)
+        return fail(WOB_INVALID_ARG, "null pointer");
+    if (!aligned16(buf) || !aligned16(sink))
+        return fail(WOB_INVALID_ARG, "pointers must be 16-byte aligned");
+    int s = arch_gate();
+    if (s != WOB_OK)
+        return s;
+    return launched(wob::launch_stream_read(buf, bytes, static_cast<uint32_t *>(sink),
+                                            static_cast<hipStream_t>(stream)),
+                    "stream read");
+}
+
 } // extern "C"

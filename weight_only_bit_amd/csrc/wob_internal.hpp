@@ -59,6 +59,10 @@ hipError_t launch_mxfp4_moe(const void *x, const int32_t *ids, const uint8_t *w_
 hipError_t launch_w4a16_dequant(const uint32_t *qweight, const void *scales, const uint32_t *qzeros,
                                 void *out, int dt, bool out_f32, int N, int K, int g,
                                 hipStream_t stream);
+// Streaming-read reference (measurement aid): reads `bytes` (a multiple of
+// 16) of `buf`; `sink` is 256 words of scratch the kernel may write.
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 hipError_t launch_mxfp4_dequant(const uint8_t *w_fp4, const uint8_t *w_scale, void *out, int N,
                                 int K, hipStream_t stream);
 
