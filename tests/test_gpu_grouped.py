@@ -98,3 +98,15 @@ def test_grouped_moe_like_full_size(wob, oracle):
                                          d["scales"][e], d["qzeros"][e], d["K"], d["g"], ms, ns)
         ok, err, bound = oracle.tolerance_ok(y[lo + ms, ns], yref)
         assert ok, (e, err, bound)
+
+
+def test_grouped_all_groups_empty_is_a_noop(wob):
+    """Every group empty (total_M = 0): nothing is written, no error."""
+    torch = torch_mod()
+    d = wl.w4a16_grouped_inputs([0, 0, 0], 64, 256, 32, wl.F16, seed=3)
+    out = torch.full((2, 64), float("nan"), dtype=torch.float16, device="cuda")
+    x = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    wob.gemm_grouped(x, dev(d["m_offsets"]), dev(d["qweight"]), dev_act(d["scales"], d["dtype"]),
+                     dev(d["qzeros"]), 32, out=out[1:1])
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()

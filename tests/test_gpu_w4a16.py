@@ -205,3 +205,16 @@ def test_stream_read_reference_runs(wob):
     wob.stream_read(buf, 4096 + 16, sink)  # a tail shorter than one grid step
     torch.cuda.synchronize()
     assert torch.all(buf == 1)
+
+
+@pytest.mark.parametrize("path_name", ["PATH_AUTO", "PATH_SKINNY", "PATH_TILED"])
+def test_empty_batch_is_a_noop(wob, path_name):
+    """M = 0 (an empty batch) returns an empty result on every path and
+    enqueues nothing."""
+    torch = torch_mod()
+    d = wl.w4a16_inputs(1, 64, 256, 32, wl.F16, seed=5)
+    t = w4a16_to_device(d)
+    x0 = t["x"][:0]
+    y = wob.gemm(x0, t["qweight"], t["scales"], t["qzeros"], 32, path=getattr(wob, path_name))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, 64)
