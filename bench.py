@@ -19,7 +19,9 @@ oracle (single-threaded C) on the full decode call.
 
 Beside each workload, `ceilings` gives references measured the same way in
 the same run: for memory-bound calls a plain streaming read of the same byte
-count (what a kernel that only reads achieves on this device), and for the
+count (what a kernel that only reads achieves on this device) and, where the
+bytes fit the Infinity Cache, the same call on one reused operand copy
+(labelled MALL-resident; never the headline); for the
 W4A16 shapes the same product through the vendor library with 16-bit
 weights (torch.mm); for MoE stage 1 a dense bf16 GEMM of the same FLOPs.
 
@@ -214,6 +216,17 @@ def bench_w4a16(wkey: str, steps: int, warmup: int):
 
     graph_ms = kern_ms = _time_steps(step, steps, warmup)
     skinny = M <= 8
+    mall = None
+    if skinny and nbytes < MALL_BYTES // 2:
+        # the same call on one operand copy: after the first call its bytes sit
+        # in the Infinity Cache (a labelled side figure, never the headline)
+        def step_hot(i):
+            b = bufs[0]
+            wob.gemm(b["x"], b["qweight"], b["scales"], b["qzeros"], g, out=ys[0])
+
+        hot_ms = _time_steps(step_hot, steps, warmup)
+        mall = dict(what="MALL-resident: one operand copy reused (Infinity Cache hits)",
+                    us=round(hot_ms * 1e3, 3), gbs=round(nbytes / (hot_ms * 1e-3) / 1e9, 1))
     res = dict(workload=w.desc, M=M, N=N, K=K, g=g, dtype=wl.DTYPE_NAMES[d["dtype"]],
                copies=copies, bytes_per_call=nbytes, flops_per_call=flops,
                us_per_call=round(graph_ms * 1e3, 3))
@@ -238,6 +251,8 @@ def bench_w4a16(wkey: str, steps: int, warmup: int):
     if skinny:
         refs.insert(0, ("stream_read", lambda: stream_read_ceiling(nbytes, steps, warmup)))
     res["ceilings"] = _ceilings(refs)
+    if mall is not None:
+        res["ceilings"]["mall_resident"] = mall
     return res, d
 
 

@@ -218,8 +218,8 @@ struct ZeroRows {
     __device__ __forceinline__ uint16_t *row(int r) const { return y + (size_t)pairs[r] * N; }
 };
 
-// One (expert tile, weight-row tile) pair per workgroup.  ACT: tiles of 256
-// output columns (256 gate rows + the matching 256 up rows), else 512.
+// One (expert tile, weight-row tile) pair per workgroup.  ACT: tiles of 128
+// output columns (128 gate rows + the matching 128 up rows), else 384.
 template <bool ACT>
 __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w_fp4,

@@ -4,9 +4,9 @@
 // One workgroup computes a TN x TM output tile (weight rows x activation
 // rows) with the shared pipeline of wob_tile.hpp: the TN weight rows are
 // dequantized once per tile, the activation rows stream through LDS, and
-// v_mfma_f32_32x32x16_{f16,bf16} does the products.  Tiles are 512 weight
-// rows by up to 128 activation rows (TILED_NB = 4 weight blocks per wave,
-// four 32-row activation blocks); the number of activation blocks actually
+// v_mfma_f32_32x32x16_{f16,bf16} does the products.  Tiles are 256 weight
+// rows by up to 256 activation rows (TILED_NB = 2 weight blocks per wave,
+// eight 32-row activation blocks); the number of activation blocks actually
 // multiplied follows the tile's row count, so a short last tile (or a short
 // group) costs only the blocks it needs.
 //
