@@ -242,3 +242,38 @@ def test_moe_decode_silu_mul(wob, oracle, T, E, topk, N, K):
     ok, err, bound = oracle.tolerance_ok(oracle.bf16_decode(ybits), oracle.silu_mul(pre))
     assert ok, f"max err {err} > bound {bound}"
     assert np.all(ybits[0, topk - 1] == 0)
+
+
+@pytest.mark.parametrize("T,N,K", [(16, 16384, 262144), (4, 131072, 32768)])
+def test_moe_expert_past_4gib(wob, oracle, T, N, K):
+    """Expert 2 of three 2 GiB experts starts 4 GiB into w_fp4, so its base
+    offset needs 64 bits (tile path at T = 16, decode path at T = 4).  Only that
+    expert is filled and named by the ids; sampled outputs are checked against
+    the one-expert problem."""
+    torch = torch_mod()
+    E = 3
+    d = wl.moe_inputs(T, 1, 1, N, K, seed=21)
+    w = torch.empty((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    s = torch.empty((E, N, K // 32), dtype=torch.uint8, device="cuda")
+    assert w[2].data_ptr() - w.data_ptr() == 1 << 32
+    w[2].copy_(torch.from_numpy(d["w_fp4"][0]))
+    s[2].copy_(torch.from_numpy(d["w_scale"][0]))
+    ids = torch.full((T, 1), 2, dtype=torch.int32, device="cuda")
+    x = dev(d["x"].view(np.int16)).view(torch.bfloat16)
+    out = torch.empty((T + 2, N), dtype=torch.bfloat16, device="cuda")
+    out.fill_(float("nan"))
+    wob.mxfp4_moe_gemm(x, ids, w, s, out=out[1:T + 1].view(T, 1, N))
+    torch.cuda.synchronize()
+    bits = host_bits(out)
+    assert np.all(is_nan_bits(bits[0], wl.BF16)) and np.all(is_nan_bits(bits[-1], wl.BF16))
+    y = oracle.bf16_decode(bits[1:-1])
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(4)
+    ts = rng.integers(0, T, 64)
+    ns = rng.integers(0, N, 64)
+    ts[:2], ns[:2] = [0, T - 1], [0, N - 1]
+    ss = np.zeros_like(ts)
+    yref = oracle.mxfp4_moe_gemm_sampled(d["x"], np.zeros((T, 1), np.int32), d["w_fp4"],
+                                         d["w_scale"], 1, 1, N, K, ts, ss, ns)
+    ok, err, bound = oracle.tolerance_ok(y[ts, ns], yref)
+    assert ok, (err, bound)

@@ -95,3 +95,23 @@ def test_config_prefill_full_size(wob, oracle):
 def test_tiled_deterministic(wob):
     d = wl.w4a16_inputs(300, 520, 1088, 32, wl.BF16, seed=2)
     assert np.array_equal(_run(wob, d, wob.PATH_TILED), _run(wob, d, wob.PATH_TILED))
+
+
+def test_tiled_codes_past_2gib(wob, oracle):
+    """2 GiB of packed codes (N = 16384, K = 262144, g = 128): byte offsets into
+    the code matrix pass 2^31 (the ABI allows up to 2^32), so an offset kept in
+    a signed 32-bit integer would fail here.  Sampled outputs, including the
+    last weight rows and both activation rows of the tile's ends."""
+    d = wl.w4a16_inputs(16, 16384, 262144, 128, wl.F16, seed=11)
+    assert d["qweight"].nbytes == 1 << 31
+    ybits = _run(wob, d, wob.PATH_TILED)
+    y = oracle.act_decode(ybits, d["dtype"])
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(3)
+    ns = np.sort(np.concatenate([[0, 8191, 8192, 16383, 16376], rng.integers(0, 16384, 59)]))
+    ms = rng.integers(0, 16, ns.size)
+    ms[-1] = 15
+    yref = oracle.w4a16_gemm_sampled(d["x"], d["dtype"], d["qweight"], d["scales"], d["qzeros"],
+                                     d["K"], d["g"], ms, ns)
+    ok, err, bound = oracle.tolerance_ok(y[ms, ns], yref)
+    assert ok, (err, bound)
