@@ -78,6 +78,24 @@ def test_weight_hand_words_and_sign_extension(oracle):
     assert codes.tolist() == [list(range(16))]
 
 
+def test_symmetric_codes_are_offset_by_eight(oracle):
+    """No zero-point tensor means z = 8: a code c dequantizes to (c - 8) * s,
+    the offset-8 codes of the q4_0 page ("qsa_prompt_attn: Q4_0 KV on tensor
+    cores (mode 4)", What: each block's codes become (code - 8) with one fp16
+    scale per 32, which may be negative).  Expected values written from that
+    statement for the hand words 0x76543210, 0xFEDCBA98 (codes 0..15)."""
+    words = np.array([[0x76543210, 0xFEDCBA98, 0x76543210, 0xFEDCBA98]], np.uint32).view(np.int32)
+    scales = np.array([[0x3C00]], np.uint16)   # fp16 1.0 for the single group of 32
+    w = oracle.w4a16_dequant(words, scales, 0, None, 1, 32, 32)
+    assert w.tolist() == [[float(c - 8) for c in list(range(16)) * 2]]
+    scales = np.array([[0xB800]], np.uint16)   # fp16 -0.5 (a negative q4_0 scale)
+    w = oracle.w4a16_dequant(words, scales, 0, None, 1, 32, 32)
+    expect = [(c - 8) * -0.5 for c in list(range(16)) * 2]
+    assert w[0].tolist() == expect
+    # code 8 gives (8 - 8) * -0.5 = -0.0: the sign of a zero product is kept
+    assert np.signbit(w[0, 8]) and np.signbit(w[0, 24])
+
+
 def test_pack_unpack_round_trip(oracle):
     rng = np.random.default_rng(3)
     N, K, G = 48, 512, 16
