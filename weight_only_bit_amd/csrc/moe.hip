@@ -69,32 +69,6 @@ MoeWs carve(void *ws, int64_t P, int64_t E)
     return w;
 }
 
-__device__ __forceinline__ int block_excl_scan(int v, int *wsum, int &total)
-{
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d);
-        if (lane >= d)
-            incl += o;
-    }
-    if (lane == 63)
-        wsum[wave] = incl;
-    __syncthreads();
-    int before = 0;
-    total = 0;
-    for (int w = 0; w < ROUTE_THREADS / 64; ++w) {
-        const int s = wsum[w];
-        if (w < wave)
-            before += s;
-        total += s;
-    }
-    __syncthreads();
-    return before + incl - v;
-}
-
 __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const int32_t *__restrict__ ids,
                                                                   int P, int E, int tm, int32_t *hdr,
                                                                   int4 *tiles, int32_t *sorted)
@@ -103,7 +77,6 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const int32_t 
     int *cnt = lds_i;             // [E + 1]
     int *off = cnt + (E + 1);     // [E + 1]
     int *toff = off + (E + 1);    // [E + 1]
-    int *wsum = toff + (E + 1);   // [16]
     const int tid = threadIdx.x;
 
     for (int e = tid; e <= E; e += ROUTE_THREADS)
@@ -117,36 +90,47 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const int32_t 
     }
     __syncthreads();
 
-    // Exclusive prefix sums of rows and of tiles over the E + 1 buckets; each
-    // thread owns a run of consecutive buckets.
-    const int per = (E + 1 + ROUTE_THREADS - 1) / ROUTE_THREADS;
-    const int e0 = min(tid * per, E + 1), e1 = min(e0 + per, E + 1);
-    int srows = 0, stiles = 0;
-    for (int e = e0; e < e1; ++e) {
-        srows += cnt[e];
-        stiles += (cnt[e] + tm - 1) / tm;
+    // Exclusive prefix sums of rows and of tiles over the E + 1 buckets, by
+    // wave 0 alone: lane l owns a run of consecutive buckets, and one
+    // wave-wide scan joins the runs (measured: two workgroup-wide scans, each
+    // with two barriers and a serial pass over the 16 wave sums, took 1.8 us).
+    if (tid < 64) {
+        const int per = (E + 1 + 63) / 64;
+        const int e0 = min(tid * per, E + 1), e1 = min(e0 + per, E + 1);
+        int srows = 0, stiles = 0;
+        for (int e = e0; e < e1; ++e) {
+            srows += cnt[e];
+            stiles += (cnt[e] + tm - 1) / tm;
+        }
+        int ir = srows, it = stiles;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int orows = __shfl_up(ir, d), otiles = __shfl_up(it, d);
+            if (tid >= d) {
+                ir += orows;
+                it += otiles;
+            }
+        }
+        int rb = ir - srows, tb = it - stiles;
+        for (int e = e0; e < e1; ++e) {
+            off[e] = rb;
+            toff[e] = tb;
+            rb += cnt[e];
+            tb += (cnt[e] + tm - 1) / tm;
+        }
+        if (tid == 63)
+            hdr[0] = it;
     }
-    int total_rows, total_tiles;
-    int rb = block_excl_scan(srows, wsum, total_rows);
-    int tb = block_excl_scan(stiles, wsum, total_tiles);
-    for (int e = e0; e < e1; ++e) {
-        off[e] = rb;
-        toff[e] = tb;
-        rb += cnt[e];
-        tb += (cnt[e] + tm - 1) / tm;
-    }
-    if (tid == 0)
-        hdr[0] = total_tiles;
     __syncthreads();
 
+    // Tile table; each bucket's count, read here by its one thread, becomes
+    // that bucket's cursor for the scatter.
     for (int e = tid; e <= E; e += ROUTE_THREADS) {
         const int c = cnt[e];
         for (int j = 0; j * tm < c; ++j)
             tiles[toff[e] + j] = int4{e, off[e] + j * tm, min(tm, c - j * tm), 0};
+        cnt[e] = 0;
     }
-    __syncthreads();
-    for (int e = tid; e <= E; e += ROUTE_THREADS)
-        cnt[e] = 0; // reused as the per-bucket cursor
     __syncthreads();
     for (int i = tid; i < P; i += ROUTE_THREADS) {
         int e = ids[i];
@@ -572,7 +556,7 @@ hipError_t launch_mxfp4_moe(const void *x, const int32_t *ids, const uint8_t *w_
                    : launch_gemv_t<false>(x, ids, w_fp4, w_scale, y, T, (int)P, topk, E, N, K,
                                           mrmax, stream);
     const MoeWs w = carve(workspace, P, E);
-    const size_t route_lds = (size_t)(3 * (E + 1) + ROUTE_THREADS / 64) * sizeof(int);
+    const size_t route_lds = (size_t)(3 * (E + 1)) * sizeof(int);
     const int tm = act ? moe_tm<true>() : moe_tm<false>();
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(ROUTE_THREADS), route_lds, stream, ids,
                        (int)P, E, tm, w.hdr, w.tiles, w.sorted);
