@@ -49,12 +49,14 @@ def test_tiled_m_sweep(wob, oracle, dtype, M):
     _check(oracle, d, _run(wob, d, wob.PATH_TILED))
 
 
+# every (N, K) with each group size that divides K
+TILED_SHAPES = [(N, K, g) for N, K in [(8, 128), (24, 32), (256, 256), (520, 1088), (1024, 384)]
+                for g in (32, 64, 128) if K % g == 0]
+
+
 @pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
-@pytest.mark.parametrize("g", [32, 64, 128])
-@pytest.mark.parametrize("N,K", [(8, 128), (24, 32), (256, 256), (520, 1088), (1024, 384)])
+@pytest.mark.parametrize("N,K,g", TILED_SHAPES)
 def test_tiled_shapes(wob, oracle, dtype, g, N, K):
-    if K % g:
-        pytest.skip("K not a multiple of g")
     d = wl.w4a16_inputs(40, N, K, g, dtype, seed=N + K + g)
     _check(oracle, d, _run(wob, d, wob.PATH_TILED))
 
