@@ -29,7 +29,9 @@
  *   y        [M][N]        activation dtype, rounded to nearest even from fp32
  *   w_fp4    [E][N][K/2]   uint8; element k is the low nibble of byte k/2 when
  *                          k is even, the high nibble when k is odd
- *   w_scale  [E][N][K/32]  uint8 E8M0 exponent b; scale = 2^(b-127)
+ *   w_scale  [E][N][K/32]  uint8 E8M0 exponent b; scale = 2^(b-127) for every
+ *                          b in 0..254 (b = 0 is 2^-127), NaN for b = 255
+ *                          (OCP MX E8M0)
  * Packed words are unsigned bit containers (logical shifts).
  *
  * Conventions shared by every entry point:
@@ -69,7 +71,7 @@ extern "C" {
 #define WOB_U4X8_I32 2 /* eight 4-bit values packed in an int32 */
 #define WOB_F32 3
 
-/* MoE stage-1 activation for mxfp4_moe_gemm_act. */
+/* MoE stage-1 activation (the `act` argument of mxfp4_moe_gemm). */
 #define WOB_ACT_NONE 0     /* pre-activation output [T][topk][N] */
 #define WOB_ACT_SILU_MUL 1 /* silu(gate) * up: output [T][topk][N/2] */
 
@@ -100,15 +102,23 @@ int wob_device_check(void);
  *    -> WOB_DTYPE (activation-dtype zero-points are refused, not reinterpreted).
  *  group_size in {32, 64, 128} (else WOB_UNSUPPORTED); K % group_size == 0,
  *    K % 32 == 0, N % 8 == 0, M >= 0, N >= 0, K >= 32, N*K/2 below 2^32
- *    (else WOB_INVALID_ARG).
+ *    (else WOB_INVALID_ARG).  When the tiled path runs (M > 8, or the skinny
+ *    kernel's LDS cannot hold M*K activations), also 2*K*min(M, 256) below
+ *    2^32 (else WOB_INVALID_ARG).
  *    M == 0 or N == 0 is a no-op returning WOB_OK.
- *  Accumulation is fp32; y is rounded to nearest even in x's dtype.
+ *  Arithmetic, fp32 accumulation in both paths: the skinny path (M <= 8)
+ *  multiplies x with the exact (q - z) (exact products) and scales each
+ *  32-wide chunk's sum by s; the tiled path multiplies x with (q - z) * s
+ *  rounded once to x's dtype.  y is rounded to nearest even in x's dtype.
  */
 int w4a16_gemm(const void *x, int x_dtype, const int32_t *qweight, const void *scales,
                int scales_dtype, const void *qzeros, int zeros_dtype, void *y, int64_t M,
                int64_t N, int64_t K, int64_t group_size, void *stream);
 
-/* As w4a16_gemm with an explicit kernel path (WOB_PATH_*). */
+/* As w4a16_gemm with an explicit kernel path (WOB_PATH_*); WOB_PATH_SKINNY
+ * with M > 8 or M*K too large for the skinny kernel's LDS gives
+ * WOB_INVALID_ARG.  Not part of the method: it lets tests and measurements
+ * run each kernel on the same inputs. */
 int w4a16_gemm_ex(const void *x, int x_dtype, const int32_t *qweight, const void *scales,
                   int scales_dtype, const void *qzeros, int zeros_dtype, void *y, int64_t M,
                   int64_t N, int64_t K, int64_t group_size, int path, void *stream);
@@ -123,70 +133,79 @@ int w4a16_gemm_ex(const void *x, int x_dtype, const int32_t *qweight, const void
  * every group are not written.  Same dtype and shape rules as w4a16_gemm.
  * Source: the grouped GEMM named on "ROCm IQ4_XS keep-quant GEMM is 8.8x
  * behind llama.cpp's WMMA path" (vllm.cpp issue 3006), section What already
- * exists; the ragged-offset reading is this library's.
+ * exists; the ragged-offset reading is this library's.  The tiled path's
+ * bound 2*K*min(total_M, 256) below 2^32 applies.
  */
 int w4a16_gemm_grouped(const void *x, int x_dtype, const int64_t *m_offsets, int64_t num_groups,
                        int64_t total_M, const int32_t *qweight, const void *scales,
                        int scales_dtype, const void *qzeros, int zeros_dtype, void *y, int64_t N,
                        int64_t K, int64_t group_size, void *stream);
 
-/* Bytes of device workspace mxfp4_moe_gemm needs for T tokens, topk slots, E experts. */
-size_t mxfp4_moe_gemm_workspace_size(int64_t T, int64_t topk, int64_t E);
+/*
+ * Bytes of device workspace mxfp4_moe_gemm needs for T tokens, topk slots, E
+ * experts (routing scratch: per-expert tiles and the pairs sorted by expert;
+ * N and K do not change it).  0 for arguments mxfp4_moe_gemm would refuse
+ * (T < 0, topk outside 1..64, E outside 1..4096, N or K negative).
+ */
+size_t mxfp4_moe_gemm_workspace_size(int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K);
 
 /*
  * MoE stage 1, BF16 x MXFP4: for token t and slot s with expert e = topk_ids[t][s],
- *   y[t][s][n] = sum_k x[t][k] * e2m1(code_e(n,k)) * 2^(w_scale[e][n][k/32] - 127)
- * (pre-activation; gate and up halves of N as stored; no routing-weight
- * multiply).  Source: MXFP4 page above, summary and Technical Details.
+ *   pre[t][s][n] = sum_k x[t][k] * e2m1(code_e(n,k)) * 2^(w_scale[e][n][k/32] - 127)
+ * (gate and up halves of N as stored; no routing-weight multiply).
+ * Source: MXFP4 page above, summary and Technical Details.
  *
- *  x [T][K] bf16; topk_ids [T][topk] int32 on the device; y [T][topk][N] bf16.
+ *  act == WOB_ACT_NONE: y [T][topk][N] bf16 = pre.
+ *  act == WOB_ACT_SILU_MUL: the N rows of each expert's W1 are a gate half
+ *    (rows 0 .. N/2-1) and an up half (rows N/2 .. N-1), and
+ *      y[t][s][n] = silu(g) * u,  g = pre[t][s][n], u = pre[t][s][N/2 + n],
+ *      silu(v) = v / (1 + e^-v),  n < N/2,
+ *    into y [T][topk][N/2] bf16 (pre stays in fp32 and is never written).
+ *    Source: MXFP4 page above, summary and Test (the stage-1 kernel's silu
+ *    activation; the gate/up split of W1 is this library's reading).
+ *    Needs N % 32 == 0.  Any other act gives WOB_INVALID_ARG.
+ *
+ *  x [T][K] bf16; topk_ids [T][topk] int32 on the device.
  *  Rows whose id lies outside [0, E) are written as zeros.
  *  K % 64 == 0 (the page's 64-wide K tile), K >= 64, N % 16 == 0, T >= 0,
  *  1 <= topk <= 64, 1 <= E <= 4096, T*K*2 and N*K/2 below 2^32 (else
  *  WOB_INVALID_ARG).
- *  workspace: device memory of at least mxfp4_moe_gemm_workspace_size(T, topk, E)
- *  bytes, 16-byte aligned (else WOB_INVALID_ARG); its contents on entry do not
- *  matter.  Calls that share one workspace must be ordered on one stream.
- *  Decode batches (T <= 8, with K <= 32768) run a memory-bound kernel that
- *  routes on its own and leaves the workspace untouched; the workspace is
- *  still required and checked.  Both kernels compute the same function.
+ *  workspace: device memory of at least mxfp4_moe_gemm_workspace_size(T, topk,
+ *  E, N, K) bytes, 16-byte aligned (else WOB_INVALID_ARG); its contents on
+ *  entry do not matter.  Calls that share one workspace must be ordered on
+ *  one stream.  Decode batches (T <= 8, with K <= 32768) run a memory-bound
+ *  kernel that routes on its own and leaves the workspace untouched; the
+ *  workspace is still required and checked.  Both kernels compute the same
+ *  function.
  */
 int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
                    const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E, int64_t N,
-                   int64_t K, void *workspace, size_t workspace_bytes, void *stream);
+                   int64_t K, int act, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * MoE stage 1 with its activation fused into the store.  act == WOB_ACT_NONE
- * is exactly mxfp4_moe_gemm.  act == WOB_ACT_SILU_MUL reads the N rows of each
- * expert's W1 as a gate half (rows 0 .. N/2-1) and an up half (rows N/2 ..
- * N-1) and writes
- *   y[t][s][n] = silu(g) * u,  g = pre[t][s][n], u = pre[t][s][N/2 + n],
- *   silu(v) = v / (1 + e^-v),  n < N/2,
- * into y [T][topk][N/2] bf16, where pre is the mxfp4_moe_gemm output (kept in
- * fp32, never written).  Source: MXFP4 page above, summary and Test (the
- * stage-1 kernel's silu activation; its gate/up split of W1 is this library's
- * reading).  Needs N % 32 == 0 for WOB_ACT_SILU_MUL; otherwise the same rules,
- * workspace and error behaviour as mxfp4_moe_gemm (an unknown act gives
- * WOB_INVALID_ARG).
- */
-int mxfp4_moe_gemm_act(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
-                       const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E,
-                       int64_t N, int64_t K, int act, void *workspace, size_t workspace_bytes,
-                       void *stream);
-
-/*
- * Dequantization probes: run the same device dequantization helpers the GEMM
- * kernels use and write the dequantized weights out[N][K].
- *  out_dtype WOB_F32: the skinny kernel's form, exactly (q - z) * s.
- *  out_dtype == scales_dtype: the MFMA operand form, (q - z) * s rounded to
- *    nearest even in that dtype.
- * Same shape and dtype rules as w4a16_gemm.
+ * Dequantization probes: write out the weights as the GEMM kernels form them,
+ * through the same device helpers, so the unpack / dequantize stage can be
+ * compared bit for bit with its definition.  Source: zero-point page above,
+ * section Testing (value-level checks against a reference dequantization, so
+ * that a wrong nibble index cannot pass silently).
+ *  out_dtype WOB_F32: the skinny kernel's exact (q - z), formed by that
+ *    kernel's helpers, times the scale in fp32 (exact; the kernel itself
+ *    applies the scale to each 32-wide chunk's sum of products).
+ *  out_dtype == scales_dtype: the tiled kernels' MFMA operand values,
+ *    (q - z) * s rounded to nearest even in that dtype.
+ * Same shape and dtype rules as w4a16_gemm (zeros_dtype, here too, must be
+ * WOB_U4X8_I32 when qzeros is given).
  */
 int w4a16_dequant(const int32_t *qweight, const void *scales, int scales_dtype,
                   const void *qzeros, int zeros_dtype, void *out, int out_dtype, int64_t N,
                   int64_t K, int64_t group_size, void *stream);
 
-/* MXFP4 probe: out[N][K] bf16 = the MoE kernel's B-operand values for one expert. */
+/*
+ * MXFP4 probe: out[N][K] bf16 = the MoE kernels' weight-operand values for
+ * one expert (E2M1 code times the E8M0 scale, as v_cvt_scalef32_pk_bf16_fp4
+ * forms them).  Source: MXFP4 page above, Technical Details.  K % 32 == 0,
+ * K >= 32, N >= 0, w_fp4 and out 16-byte aligned (else WOB_INVALID_ARG).
+ */
 int mxfp4_dequant(const uint8_t *w_fp4, const uint8_t *w_scale, void *out, int64_t N, int64_t K,
                   void *stream);
 

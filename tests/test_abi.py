@@ -87,6 +87,20 @@ def test_shape_checks(L):
     assert _gemm(L, N=0) == L.OK
 
 
+def test_tiled_activation_offsets_bound(L):
+    """The tile kernels keep a tile's activation row offsets in 32 bits: a long
+    K with a full 256-row tile is refused (2*K*min(M, 256) must stay below
+    2^32), on the dense and the grouped form.  (Every call here must be refused
+    before any device access: the pointers are host stand-ins.)"""
+    K = 1 << 23  # 2*K*256 = 2^32
+    assert _gemm(L, M=256, N=8, K=K, g=128) == L.INVALID_ARG
+    assert "tiled path" in L.last_error()
+    f = _Fake()
+    p = f.p
+    grouped = L.lib().w4a16_gemm_grouped(p, 0, p, 2, 512, p, p, 0, p, 2, p, 8, K, 128, None)
+    assert grouped == L.INVALID_ARG
+
+
 def test_misaligned_pointer_refused(L):
     f = _Fake()
     bad = ctypes.c_void_p(f.p.value + 2)
@@ -97,15 +111,17 @@ def test_misaligned_pointer_refused(L):
 def test_moe_checks(L):
     f = _Fake()
     p = f.p
-    need = L.lib().mxfp4_moe_gemm_workspace_size(1024, 4, 32)
+    need = L.lib().mxfp4_moe_gemm_workspace_size(1024, 4, 32, 5760, 2880)
     assert need > 0
-    assert L.lib().mxfp4_moe_gemm_workspace_size(-1, 4, 32) == 0
-    call = lambda K=64, N=32, ws=need, T=4: L.lib().mxfp4_moe_gemm(p, p, p, p, p, T, 4, 32, N, K, p, ws, None)
+    assert L.lib().mxfp4_moe_gemm_workspace_size(-1, 4, 32, 64, 64) == 0
+    assert L.lib().mxfp4_moe_gemm_workspace_size(4, 65, 32, 64, 64) == 0
+    call = lambda K=64, N=32, ws=need, T=4: L.lib().mxfp4_moe_gemm(p, p, p, p, p, T, 4, 32, N, K,
+                                                                   0, p, ws, None)
     assert call(K=48) == L.INVALID_ARG
     assert call(K=96) == L.INVALID_ARG  # the K tile is 64 wide
     assert call(N=24) == L.INVALID_ARG
     assert call(T=1 << 21, K=1 << 11) == L.INVALID_ARG  # x past 32-bit byte offsets
-    act = lambda a, N=32: L.lib().mxfp4_moe_gemm_act(p, p, p, p, p, 4, 4, 32, N, 64, a, p, need, None)
+    act = lambda a, N=32: L.lib().mxfp4_moe_gemm(p, p, p, p, p, 4, 4, 32, N, 64, a, p, need, None)
     assert act(2) == L.INVALID_ARG          # unknown activation
     assert act(1, N=48) == L.INVALID_ARG    # silu(gate) * up needs N % 32 == 0
     assert call(ws=0) == L.INVALID_ARG
@@ -142,3 +158,76 @@ def test_no_gpu_means_an_error_not_a_fallback(L):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _gemm(L) in (L.HIP, L.UNSUPPORTED)
+
+
+# --- Python binding: operand shapes and dtypes are checked before any device access ---
+
+@pytest.fixture(scope="module")
+def wobpkg(L):
+    import weight_only_bit_amd as w
+    return w
+
+
+def _w4_cpu(M=4, N=16, K=64, g=32, dtype=None):
+    import torch
+    dt = dtype or torch.float16
+    G = K // g
+    return dict(x=torch.zeros((M, K), dtype=dt), q=torch.zeros((N, K // 8), dtype=torch.int32),
+                s=torch.zeros((N, G), dtype=dt), z=torch.zeros((N // 8, G), dtype=torch.int32))
+
+
+def test_binding_gemm_shape_checks(wobpkg):
+    import torch
+    t = _w4_cpu()
+    with pytest.raises(ValueError, match="scales"):   # scales for another group size
+        wobpkg.gemm(t["x"], t["q"], torch.zeros((16, 4), dtype=torch.float16), t["z"], 32)
+    with pytest.raises(ValueError, match="qweight"):  # qweight for another K
+        wobpkg.gemm(t["x"], torch.zeros((16, 4), dtype=torch.int32), t["s"], t["z"], 32)
+    with pytest.raises(ValueError, match="qzeros"):
+        wobpkg.gemm(t["x"], t["q"], t["s"], torch.zeros((1, 1), dtype=torch.int32), 32)
+    with pytest.raises(ValueError, match="out"):      # too small an output
+        wobpkg.gemm(t["x"], t["q"], t["s"], t["z"], 32, out=torch.empty((4, 8), dtype=torch.float16))
+    with pytest.raises(TypeError, match="out"):
+        wobpkg.gemm(t["x"], t["q"], t["s"], t["z"], 32, out=torch.empty((4, 16), dtype=torch.float32))
+    with pytest.raises(TypeError, match="scales"):
+        wobpkg.gemm(t["x"], t["q"], t["s"].to(torch.bfloat16), t["z"], 32)
+    with pytest.raises(TypeError, match="qzeros"):    # activation-dtype zero-points
+        wobpkg.gemm(t["x"], t["q"], t["s"], torch.zeros((16, 2), dtype=torch.float16), 32)
+    with pytest.raises(ValueError, match="group_size"):
+        wobpkg.gemm(t["x"], t["q"], t["s"], t["z"], 48)
+    with pytest.raises(ValueError, match="device"):   # shapes right: then the device check
+        wobpkg.gemm(t["x"], t["q"], t["s"], t["z"], 32)
+
+
+def test_binding_grouped_and_moe_shape_checks(wobpkg):
+    import torch
+    x = torch.zeros((10, 64), dtype=torch.float16)
+    q = torch.zeros((3, 16, 8), dtype=torch.int32)
+    s = torch.zeros((3, 16, 2), dtype=torch.float16)
+    z = torch.zeros((3, 2, 2), dtype=torch.int32)
+    off = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(ValueError, match="m_offsets"):
+        wobpkg.gemm_grouped(x, torch.zeros(3, dtype=torch.int64), q, s, z, 32)
+    with pytest.raises(ValueError, match="scales"):
+        wobpkg.gemm_grouped(x, off, q, s[:2], z, 32)
+    with pytest.raises(ValueError, match="device"):
+        wobpkg.gemm_grouped(x, off, q, s, z, 32)
+    xb = torch.zeros((4, 128), dtype=torch.bfloat16)
+    ids = torch.zeros((4, 2), dtype=torch.int32)
+    w = torch.zeros((3, 32, 64), dtype=torch.uint8)
+    ws = torch.zeros((3, 32, 4), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="w_scale"):
+        wobpkg.mxfp4_moe_gemm(xb, ids, w, ws[:, :, :3])
+    with pytest.raises(ValueError, match="out"):
+        wobpkg.mxfp4_moe_gemm(xb, ids, w, ws, out=torch.empty((4, 2, 32), dtype=torch.bfloat16),
+                              act=wobpkg.ACT_SILU_MUL)
+    with pytest.raises(TypeError, match="topk_ids"):
+        wobpkg.mxfp4_moe_gemm(xb, ids.to(torch.int64), w, ws)
+    with pytest.raises(ValueError, match="workspace"):
+        wobpkg.mxfp4_moe_gemm(xb, ids, w, ws, workspace=torch.zeros(4, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="activation"):
+        wobpkg.mxfp4_moe_gemm(xb, ids, w, ws, act=5)
+    with pytest.raises(ValueError, match="device"):
+        wobpkg.mxfp4_moe_gemm(xb, ids, w, ws)
+    with pytest.raises(ValueError, match="w_scale"):
+        wobpkg.mxfp4_dequant(w[0], ws[0, :, :2])

@@ -63,6 +63,15 @@ def test_grouped_many_groups_symmetric(wob, oracle, dtype):
     _check(oracle, d, _run(wob, d, symmetric=True), symmetric=True)
 
 
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+def test_grouped_q4_0_arithmetic(wob, oracle, dtype):
+    """Symmetric codes (z = 8) with signed two-decade scales at g = 32 on the
+    grouped path (the Q4_0 KV page's sections What and Signed scales)."""
+    d = wl.w4a16_grouped_inputs([37, 0, 300, 5], 264, 544, 32, dtype, seed=8, symmetric=True,
+                                signed_scales=True)
+    _check(oracle, d, _run(wob, d, symmetric=True), symmetric=True)
+
+
 def test_grouped_single_group_matches_dense(wob):
     """One group covering every row gives the dense GEMM's bits."""
     torch = torch_mod()

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
+from tests import oracle_threads
 from tests.gpu_util import dev, host_bits, is_nan_bits, require_gpu, torch_mod
 
 pytestmark = pytest.mark.gpu
@@ -116,21 +117,39 @@ def test_moe_deterministic(wob):
     assert np.array_equal(_run(wob, d), _run(wob, d))
 
 
+def _moe_tile_samples(d, rng, width=128, per=4):
+    """(token, slot, n) samples covering every (expert, column block) pair:
+    for each expert its first and last routed pair and `per` - 2 random ones,
+    each at both edges and two random columns of every `width`-wide block."""
+    T, topk, N, E = d["T"], d["topk"], d["N"], d["E"]
+    pairs = d["ids"].reshape(-1)
+    ts, ss, ns = [], [], []
+    for e in range(E):
+        ps = np.flatnonzero(pairs == e)
+        if ps.size == 0:
+            continue
+        pick = np.concatenate([[ps[0], ps[-1]], rng.choice(ps, per - 2)])
+        for c0 in range(0, N, width):
+            cols = c0 + np.concatenate([[0, min(width, N - c0) - 1],
+                                        rng.integers(0, min(width, N - c0), 2)])
+            for p in pick:
+                ts.append(np.full(cols.size, p // topk))
+                ss.append(np.full(cols.size, p % topk))
+                ns.append(cols)
+    return np.concatenate(ts), np.concatenate(ss), np.concatenate(ns)
+
+
 def test_config_moe_stage1_full_size(wob, oracle):
-    """1024 tokens, 32 experts, top-4, K=2880, N=5760: every output finite, 3000
-    sampled (token, slot, n) outputs against the oracle."""
+    """1024 tokens, 32 experts, top-4, K=2880, N=5760 in the benchmark's launch
+    configuration: every output finite, and for every expert and every
+    128-column block, four of its routed rows at four columns each (both
+    block edges) against the oracle."""
     d = wl.BY_KEY["moe_stage1"].make()
     ybits = _run(wob, d)
     y = oracle.bf16_decode(ybits)
     assert np.all(np.isfinite(y))
-    rng = np.random.default_rng(0)
-    T, topk, N = d["T"], d["topk"], d["N"]
-    ts = rng.integers(0, T, 3000)
-    ss = rng.integers(0, topk, 3000)
-    ns = rng.integers(0, N, 3000)
-    ts[:3], ss[:3], ns[:3] = [0, T - 1, 5], [0, topk - 1, 1], [0, N - 1, 5759 - 128]
-    yref = oracle.mxfp4_moe_gemm_sampled(d["x"], d["ids"], d["w_fp4"], d["w_scale"], topk, d["E"],
-                                         N, d["K"], ts, ss, ns)
+    ts, ss, ns = _moe_tile_samples(d, np.random.default_rng(0))
+    yref = oracle_threads.mxfp4_moe_gemm_sampled(oracle, d, ts, ss, ns)
     # the bound takes the sampled outputs' max|y_ref|: no looser than the global one
     ok, err, bound = oracle.tolerance_ok(y[ts, ss, ns], yref)
     assert ok, (err, bound)

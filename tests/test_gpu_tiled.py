@@ -3,12 +3,15 @@
 Covers every tile height (M up to 32, 64, 128, above), ragged M, N and K
 tails (N not a multiple of the 256-row tile, K not a multiple of the 128 span),
 g in {32, 64, 128}, fp16/bf16, symmetric codes and signed two-decade scales,
-plus the full prefill shape 2048x16384x5376 (g=128) on sampled outputs.
+the q4_0 combination of both at g = 32, weights that dequantize to zeros under
+activations with outliers, plus the full prefill shape 2048x16384x5376 (g=128)
+on sampled outputs from every output tile.
 """
 import numpy as np
 import pytest
 
 import workloads as wl
+from tests import oracle_threads
 from tests.gpu_util import host_bits, is_nan_bits, require_gpu, torch_mod, w4a16_to_device
 
 pytestmark = pytest.mark.gpu
@@ -69,6 +72,29 @@ def test_tiled_symmetric_and_signed(wob, oracle, dtype):
     _check(oracle, d, _run(wob, d, wob.PATH_TILED))
 
 
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("M", [40, 300])
+def test_tiled_q4_0_arithmetic(wob, oracle, dtype, M):
+    """Codes offset by 8 with signed two-decade scales, one per 32 (the Q4_0 KV
+    page's sections What and Signed scales), on the MFMA path, with N and K
+    tails (520 rows, K = 1088)."""
+    d = wl.w4a16_inputs(M, 520, 1088, 32, dtype, seed=M + 9, symmetric=True, signed_scales=True)
+    _check(oracle, d, _run(wob, d, wob.PATH_TILED))
+
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("live", [0.0, 0.01])
+def test_tiled_degenerate_weights_outlier_activations(wob, oracle, dtype, live):
+    """Weights that dequantize to zero in most (or all) groups under activations
+    with +-1e2..1e3 outlier columns; all-zero weights give all-zero outputs."""
+    d = wl.w4a16_degenerate_inputs(70, 264, 2080, 32, dtype, seed=int(live * 100) + dtype,
+                                   live_groups=live)
+    ybits = _run(wob, d, wob.PATH_TILED)
+    _check(oracle, d, ybits)
+    if live == 0.0:
+        assert np.all(oracle.act_decode(ybits, dtype) == 0.0)
+
+
 def test_tiled_matches_skinny_on_small_m(wob):
     """Both paths on the same M <= 8 input agree to the parity bound of each other."""
     d = wl.w4a16_inputs(4, 512, 1024, 128, wl.F16, seed=3)
@@ -78,18 +104,25 @@ def test_tiled_matches_skinny_on_small_m(wob):
 
 
 def test_config_prefill_full_size(wob, oracle):
-    """2048x16384x5376 g=128 fp16: all outputs finite; 3000 sampled outputs
-    spread over every row/column tile against the oracle."""
+    """2048x16384x5376 g=128 fp16 in the benchmark's launch configuration: all
+    outputs finite; 16 sampled outputs in each of the 8 x 64 output tiles
+    (256 x 256), including each tile's four corners, against the oracle."""
     d = wl.BY_KEY["prefill"].make()
     ybits = _run(wob, d, wob.PATH_AUTO)
     y = oracle.act_decode(ybits, d["dtype"])
     assert np.all(np.isfinite(y))
     rng = np.random.default_rng(0)
-    ns = np.sort(np.concatenate([[0, 255, 256, d["N"] - 1], rng.integers(0, d["N"], 2996)]))
-    ms = rng.integers(0, d["M"], ns.size)
-    ms[:4] = [0, 2047, 255, 256]
-    yref = oracle.w4a16_gemm_sampled(d["x"], d["dtype"], d["qweight"], d["scales"], d["qzeros"],
-                                     d["K"], d["g"], ms, ns)
+    ms, ns = [], []
+    for mt in range(d["M"] // 256):
+        for nt in range(d["N"] // 256):
+            m = mt * 256 + np.concatenate([[0, 0, 255, 255], rng.integers(0, 256, 12)])
+            n = nt * 256 + np.concatenate([[0, 255, 0, 255], rng.integers(0, 256, 12)])
+            ms.append(m)
+            ns.append(n)
+    ms, ns = np.concatenate(ms), np.concatenate(ns)
+    order = np.argsort(ns, kind="stable")
+    ms, ns = ms[order], ns[order]
+    yref = oracle_threads.w4a16_gemm_sampled(oracle, d, ms, ns)
     ok, err, bound = oracle.tolerance_ok(y[ms, ns], yref)
     assert ok, (err, bound)
 

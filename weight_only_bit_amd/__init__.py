@@ -63,6 +63,47 @@ def _check_device(*tensors):
     return dev
 
 
+# Shape and dtype checks.  They read only .shape and .dtype, so they run
+# before any device access (and work on CPU or meta tensors): the C ABI sees
+# raw pointers and could not detect an operand smaller than its shape says.
+
+def _want(t, name, shape, dtypes):
+    """t must exist, have exactly `shape`, and one of `dtypes`."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected one of {[str(d) for d in dtypes]}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+
+
+def _act_dtypes():
+    torch = _torch()
+    return (torch.float16, torch.bfloat16)
+
+
+def _w4_group_count(K: int, group_size: int) -> int:
+    if group_size <= 0 or K % group_size != 0:
+        raise ValueError(f"K={K} is not a multiple of group_size={group_size}")
+    return K // group_size
+
+
+def _check_w4_weights(qweight, scales, qzeros, N, K, group_size, act, lead=()):
+    """qweight [*lead, N, K/8] int32; scales [*lead, N, K/g] act; qzeros
+    [*lead, N/8, K/g] int32 or None (activation-dtype zero-points are refused)."""
+    torch = _torch()
+    if K % 8 != 0 or N % 8 != 0:
+        raise ValueError(f"K={K} and N={N} must be multiples of 8")
+    G = _w4_group_count(K, group_size)
+    _want(qweight, "qweight", (*lead, N, K // 8), (torch.int32,))
+    _want(scales, "scales", (*lead, N, G), (act,))
+    if qzeros is not None:
+        if qzeros.dtype != torch.int32:
+            raise TypeError(f"qzeros must be packed 4-bit zero-points (int32); dtype {qzeros.dtype} "
+                            "is refused, not reinterpreted")
+        _want(qzeros, "qzeros", (*lead, N // 8, G), (torch.int32,))
+
+
 def device_check() -> None:
     """Raise unless the current device is gfx950."""
     _lib.check(_lib.lib().wob_device_check(), "device_check")
@@ -72,13 +113,18 @@ def gemm(x, qweight, scales, qzeros, group_size: int, out=None, path: int = PATH
     """W4A16 GEMM: y[M,N] = x[M,K] . ((q - z) * s)^T.
 
     x [M,K] fp16/bf16; qweight [N,K/8] int32; scales [N,K/g] x.dtype;
-    qzeros [N/8,K/g] int32 (packed) or None (symmetric, z = 8).
+    qzeros [N/8,K/g] int32 (packed) or None (symmetric, z = 8); out [M,N] x.dtype.
     """
     torch = _torch()
+    if x.dim() != 2 or qweight.dim() != 2:
+        raise ValueError("x must be [M, K] and qweight [N, K/8]")
+    _want(x, "x", tuple(x.shape), _act_dtypes())
     M, K = x.shape
     N = qweight.shape[0]
+    _check_w4_weights(qweight, scales, qzeros, N, K, group_size, x.dtype)
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _want(out, "out", (M, N), (x.dtype,))
     dev = _check_device(x, qweight, scales, qzeros, out)
     with torch.cuda.device(dev):
         st = _lib.lib().w4a16_gemm_ex(
@@ -90,14 +136,20 @@ def gemm(x, qweight, scales, qzeros, group_size: int, out=None, path: int = PATH
 
 
 def gemm_grouped(x, m_offsets, qweight, scales, qzeros, group_size: int, out=None):
-    """Ragged grouped W4A16 GEMM; m_offsets is a device int64 tensor [E+1]."""
+    """Ragged grouped W4A16 GEMM: x [total_M,K]; m_offsets device int64 [E+1];
+    qweight [E,N,K/8] int32; scales [E,N,K/g]; qzeros [E,N/8,K/g] int32 or None;
+    out [total_M,N] x.dtype."""
     torch = _torch()
+    if x.dim() != 2 or qweight.dim() != 3:
+        raise ValueError("x must be [total_M, K] and qweight [E, N, K/8]")
+    _want(x, "x", tuple(x.shape), _act_dtypes())
     total_m, K = x.shape
     E, N = qweight.shape[0], qweight.shape[1]
-    if m_offsets.dtype != torch.int64 or m_offsets.numel() != E + 1:
-        raise ValueError("m_offsets must be int64 with num_groups + 1 entries")
+    _check_w4_weights(qweight, scales, qzeros, N, K, group_size, x.dtype, lead=(E,))
+    _want(m_offsets, "m_offsets", (E + 1,), (torch.int64,))
     if out is None:
         out = torch.empty((total_m, N), dtype=x.dtype, device=x.device)
+    _want(out, "out", (total_m, N), (x.dtype,))
     dev = _check_device(x, m_offsets, qweight, scales, qzeros, out)
     with torch.cuda.device(dev):
         st = _lib.lib().w4a16_gemm_grouped(
@@ -108,33 +160,45 @@ def gemm_grouped(x, m_offsets, qweight, scales, qzeros, group_size: int, out=Non
     return out
 
 
-def moe_workspace_size(T: int, topk: int, E: int) -> int:
-    return int(_lib.lib().mxfp4_moe_gemm_workspace_size(T, topk, E))
+def moe_workspace_size(T: int, topk: int, E: int, N: int = 0, K: int = 0) -> int:
+    """Bytes of workspace mxfp4_moe_gemm needs (0 for arguments it refuses)."""
+    return int(_lib.lib().mxfp4_moe_gemm_workspace_size(T, topk, E, N, K))
 
 
 def mxfp4_moe_gemm(x, topk_ids, w_fp4, w_scale, out=None, workspace=None, act: int = ACT_NONE):
     """MoE stage 1: x [T,K] bf16, topk_ids [T,topk] int32, w_fp4 [E,N,K/2] uint8 and
     w_scale [E,N,K/32] uint8 (E8M0) -> y [T,topk,N] bf16 (act=ACT_NONE) or
-    y [T,topk,N/2] = silu(gate) * up (act=ACT_SILU_MUL)."""
+    y [T,topk,N/2] = silu(gate) * up (act=ACT_SILU_MUL).  workspace: device memory of
+    at least moe_workspace_size(T, topk, E, N, K) bytes (allocated when None)."""
     torch = _torch()
+    if x.dim() != 2 or topk_ids.dim() != 2 or w_fp4.dim() != 3:
+        raise ValueError("x must be [T, K], topk_ids [T, topk] and w_fp4 [E, N, K/2]")
+    _want(x, "x", tuple(x.shape), (torch.bfloat16,))
     T, K = x.shape
     topk = topk_ids.shape[1]
     E, N = w_fp4.shape[0], w_fp4.shape[1]
-    if x.dtype != torch.bfloat16 or topk_ids.dtype != torch.int32:
-        raise TypeError("x must be bfloat16 and topk_ids int32")
-    if w_fp4.dtype != torch.uint8 or w_scale.dtype != torch.uint8:
-        raise TypeError("w_fp4 and w_scale must be uint8")
+    if K % 32 != 0:
+        raise ValueError(f"K={K} must be a multiple of 32 (one E8M0 scale per 32)")
+    _want(topk_ids, "topk_ids", (T, topk), (torch.int32,))
+    _want(w_fp4, "w_fp4", (E, N, K // 2), (torch.uint8,))
+    _want(w_scale, "w_scale", (E, N, K // 32), (torch.uint8,))
+    if act not in (ACT_NONE, ACT_SILU_MUL):
+        raise ValueError(f"unknown activation {act}")
+    nout = N // 2 if act == ACT_SILU_MUL else N
     if out is None:
-        nout = N // 2 if act == ACT_SILU_MUL else N
         out = torch.empty((T, topk, nout), dtype=torch.bfloat16, device=x.device)
-    need = moe_workspace_size(T, topk, E)
+    _want(out, "out", (T, topk, nout), (torch.bfloat16,))
+    need = moe_workspace_size(T, topk, E, N, K)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if ws_bytes < need:
+        raise ValueError(f"workspace holds {ws_bytes} bytes; {need} are needed")
     dev = _check_device(x, topk_ids, w_fp4, w_scale, out, workspace)
     with torch.cuda.device(dev):
-        st = _lib.lib().mxfp4_moe_gemm_act(
+        st = _lib.lib().mxfp4_moe_gemm(
             _ptr(x), _ptr(topk_ids), _ptr(w_fp4), _ptr(w_scale), _ptr(out), T, topk, E, N, K, act,
-            _ptr(workspace), workspace.numel(), _stream(dev))
+            _ptr(workspace), ws_bytes, _stream(dev))
     _lib.check(st, "mxfp4_moe_gemm")
     return out
 
@@ -143,9 +207,15 @@ def w4a16_dequant(qweight, scales, qzeros, group_size: int, out_dtype=None):
     """Probe: the kernels' dequantized weights [N,K] (float32 skinny form, or
     the scales' dtype for the MFMA operand form)."""
     torch = _torch()
-    N = qweight.shape[0]
-    K = qweight.shape[1] * 8
+    if qweight.dim() != 2:
+        raise ValueError("qweight must be [N, K/8]")
+    N, K = qweight.shape[0], qweight.shape[1] * 8
+    if scales.dtype not in _act_dtypes():
+        raise TypeError(f"scales must be float16 or bfloat16, not {scales.dtype}")
+    _check_w4_weights(qweight, scales, qzeros, N, K, group_size, scales.dtype)
     out_dtype = out_dtype or torch.float32
+    if out_dtype not in (torch.float32, scales.dtype):
+        raise TypeError("out_dtype must be float32 or the scales' dtype")
     out = torch.empty((N, K), dtype=out_dtype, device=qweight.device)
     dev = _check_device(qweight, scales, qzeros, out)
     with torch.cuda.device(dev):
@@ -158,10 +228,15 @@ def w4a16_dequant(qweight, scales, qzeros, group_size: int, out_dtype=None):
 
 
 def mxfp4_dequant(w_fp4, w_scale):
-    """Probe: the MoE kernel's bf16 B-operand values [N,K] for one expert."""
+    """Probe: the MoE kernels' bf16 weight-operand values [N,K] for one expert."""
     torch = _torch()
-    N = w_fp4.shape[0]
-    K = w_fp4.shape[1] * 2
+    if w_fp4.dim() != 2:
+        raise ValueError("w_fp4 must be [N, K/2]")
+    N, K = w_fp4.shape[0], w_fp4.shape[1] * 2
+    if K % 32 != 0:
+        raise ValueError(f"K={K} must be a multiple of 32")
+    _want(w_fp4, "w_fp4", (N, K // 2), (torch.uint8,))
+    _want(w_scale, "w_scale", (N, K // 32), (torch.uint8,))
     out = torch.empty((N, K), dtype=torch.bfloat16, device=w_fp4.device)
     dev = _check_device(w_fp4, w_scale, out)
     with torch.cuda.device(dev):
@@ -174,9 +249,9 @@ def stream_read(buf, nbytes: int, sink) -> None:
     """Measurement aid: read nbytes of the device tensor buf once (the device's
     streaming-read reference for a byte count); sink: >= 1024 bytes of scratch."""
     torch = _torch()
-    dev = _check_device(buf, sink)
     if nbytes > buf.numel() * buf.element_size() or sink.numel() * sink.element_size() < 1024:
         raise ValueError("buffer smaller than nbytes or sink under 1024 bytes")
+    dev = _check_device(buf, sink)
     with torch.cuda.device(dev):
         st = _lib.lib().wob_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(dev))
     _lib.check(st, "wob_stream_read")

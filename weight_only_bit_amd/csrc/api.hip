@@ -103,6 +103,19 @@ int check_w4(const void *x, int x_dtype, const int32_t *qweight, const void *sca
     return WOB_OK;
 }
 
+// The tile kernels address a tile's activation rows with 32-bit byte offsets
+// from the tile's first row: up to 2 K (rows - 1) plus a row's last 16 bytes,
+// rows <= 256.  Refuse shapes whose offsets would not fit.
+int check_tile_offsets(int64_t M, int64_t K)
+{
+    const int64_t rows = M < 256 ? M : 256;
+    if (rows > 0 && 2 * K * rows > (int64_t)UINT32_MAX)
+        return fail(WOB_INVALID_ARG,
+                    "K=%lld too long for the tiled path (2*K*min(M,256) must stay below 2^32)",
+                    (long long)K);
+    return WOB_OK;
+}
+
 wob::W4Args make_args(const void *x, int dt, const int32_t *qweight, const void *scales,
                       const void *qzeros, void *y, int64_t M, int64_t N, int64_t K, int64_t g)
 {
@@ -158,12 +171,16 @@ int w4a16_gemm_ex(const void *x, int x_dtype, const int32_t *qweight, const void
         return fail(WOB_INVALID_ARG, "skinny path needs M <= 8 and M*K small enough for LDS");
     if (M == 0 || N == 0)
         return ok();
+    const bool skinny = path == WOB_PATH_SKINNY ||
+                        (path == WOB_PATH_AUTO &&
+                         wob::skinny_fits((int)M, (int)N, (int)K, (int)group_size));
+    if (!skinny && (s = check_tile_offsets(M, K)) != WOB_OK)
+        return s;
     s = arch_gate();
     if (s != WOB_OK)
         return s;
     wob::W4Args a = make_args(x, x_dtype, qweight, scales, qzeros, y, M, N, K, group_size);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool skinny = path == WOB_PATH_SKINNY || (path == WOB_PATH_AUTO && wob::skinny_fits(a.M, a.N, a.K, a.g));
     if (skinny)
         return launched(wob::launch_w4a16_skinny(a, st), "w4a16 skinny");
     return launched(wob::launch_w4a16_tiled(a, st), "w4a16 tiled");
@@ -192,6 +209,8 @@ int w4a16_gemm_grouped(const void *x, int x_dtype, const int64_t *m_offsets, int
         return ok();
     if (!m_offsets || !aligned16(m_offsets))
         return fail(WOB_INVALID_ARG, "m_offsets must be a 16-byte aligned device pointer");
+    if ((s = check_tile_offsets(total_M, K)) != WOB_OK)
+        return s;
     s = arch_gate();
     if (s != WOB_OK)
         return s;
@@ -201,18 +220,24 @@ int w4a16_gemm_grouped(const void *x, int x_dtype, const int64_t *m_offsets, int
                     "w4a16 grouped");
 }
 
-size_t mxfp4_moe_gemm_workspace_size(int64_t T, int64_t topk, int64_t E)
+size_t mxfp4_moe_gemm_workspace_size(int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K)
 {
-    if (T < 0 || topk < 1 || E < 1)
+    // The routing scratch depends on the pair count and the experts only.
+    if (T < 0 || topk < 1 || E < 1 || N < 0 || K < 0 || T > INT_MAX / 64 || topk > 64 ||
+        E > 4096)
         return 0;
     return wob::moe_workspace_bytes(T, topk, E);
 }
 
-int mxfp4_moe_gemm_act(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
-                       const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E,
-                       int64_t N, int64_t K, int act, void *workspace, size_t workspace_bytes,
-                       void *stream)
+namespace {
+
+// MoE argument checks shared by both MoE entry points (everything but the
+// workspace).  Sets *noop when the problem is empty.
+int check_moe(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4, const uint8_t *w_scale,
+              const void *y, int64_t T, int64_t topk, int64_t E, int64_t N, int64_t K, int act,
+              bool *noop)
 {
+    *noop = false;
     if (act != WOB_ACT_NONE && act != WOB_ACT_SILU_MUL)
         return fail(WOB_INVALID_ARG, "unknown activation %d", act);
     if (T < 0 || topk < 1 || E < 1 || N < 0 || K < 32)
@@ -230,32 +255,41 @@ int mxfp4_moe_gemm_act(const void *x, const int32_t *topk_ids, const uint8_t *w_
         T * K * 2 > (int64_t)UINT32_MAX || N * (K / 2) > (int64_t)UINT32_MAX ||
         E * N * (K / 2) > ((int64_t)1 << 40))
         return fail(WOB_INVALID_ARG, "shape too large");
-    if (T == 0 || N == 0)
-        return ok();
+    if (T == 0 || N == 0) {
+        *noop = true;
+        return WOB_OK;
+    }
     if (!x || !topk_ids || !w_fp4 || !w_scale || !y)
         return fail(WOB_INVALID_ARG, "null operand pointer");
     if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(w_fp4) || !aligned16(w_scale) ||
         !aligned16(y))
         return fail(WOB_INVALID_ARG, "operand pointers must be 16-byte aligned");
+    return WOB_OK;
+}
+
+} // namespace
+
+int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
+                   const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E, int64_t N,
+                   int64_t K, int act, void *workspace, size_t workspace_bytes, void *stream)
+{
+    bool noop;
+    int s = check_moe(x, topk_ids, w_fp4, w_scale, y, T, topk, E, N, K, act, &noop);
+    if (s != WOB_OK)
+        return s;
+    if (noop)
+        return ok();
     const size_t need = wob::moe_workspace_bytes(T, topk, E);
     if (!workspace || !aligned16(workspace) || workspace_bytes < need)
         return fail(WOB_INVALID_ARG, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need,
                     workspace_bytes);
-    int s = arch_gate();
+    s = arch_gate();
     if (s != WOB_OK)
         return s;
     return launched(wob::launch_mxfp4_moe(x, topk_ids, w_fp4, w_scale, y, (int)T, (int)topk,
                                           (int)E, (int)N, (int)K, act, workspace,
                                           static_cast<hipStream_t>(stream)),
                     "mxfp4 moe");
-}
-
-int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
-                   const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E, int64_t N,
-                   int64_t K, void *workspace, size_t workspace_bytes, void *stream)
-{
-    return mxfp4_moe_gemm_act(x, topk_ids, w_fp4, w_scale, y, T, topk, E, N, K, WOB_ACT_NONE,
-                              workspace, workspace_bytes, stream);
 }
 
 int w4a16_dequant(const int32_t *qweight, const void *scales, int scales_dtype,

@@ -2,8 +2,10 @@
 // form them in registers, using the same helpers (wob_device.hpp), so the
 // unpack/dequant stage can be compared bit for bit with the definition.
 //
-//  * W4A16, fp32 form: the skinny kernel's biased pair (B + q) minus (B + z),
-//    exact in fp32, times the fp32 scale.
+//  * W4A16, fp32 form: the skinny kernel's exact (q - z) pairs (the helpers
+//    that kernel calls) times the fp32 scale.  The kernel itself scales each
+//    chunk's sum of products rather than each weight; the product (q - z) * s
+//    is exact in fp32, so this form is the definition's value either way.
 //  * W4A16, activation form: the tiled kernels' MFMA weight-operand values
 //    (w4_word_act8, the helper those kernels call).
 //  * MXFP4: the MoE kernel's B-operand values.
@@ -32,22 +34,28 @@ __global__ __launch_bounds__(256) void w4a16_dequant_kernel(
     const uint16_t sbits = scales[(size_t)n * G + j];
     float vals[8];
     if constexpr (OUT_F32) {
+        // the skinny kernel's exact (q - z) pairs (word order, its helpers),
+        // times the scale in fp32 here: that kernel applies the scale to each
+        // chunk's sum of products instead, and (q - z) * s is exact either way
         const float s = act_to_f32<DT>(sbits);
-        const u32x4 b = nib_pairs_biased(w, DT == DT_F16 ? MAGIC4_F16 : MAGIC4_BF16);
-        const float bias = (DT == DT_F16 ? 1024.f : 128.f) + (float)z;
+        u32x4 d;
+        if constexpr (DT == DT_F16)
+            d = w4_diff_pairs_f16(w, f16_neg_bias2(z));
+        else
+            d = w4_diff_pairs_bf16(w, (float)z);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             float lo, hi;
             if constexpr (DT == DT_F16) {
-                const half2_t h = bitcast<half2_t>(b[p]);
+                const half2_t h = bitcast<half2_t>(d[p]);
                 lo = (float)h.x;
                 hi = (float)h.y;
             } else {
-                lo = bitcast<float>(b[p] << 16);
-                hi = bitcast<float>(b[p] & 0xFFFF0000u);
+                lo = bitcast<float>(d[p] << 16);
+                hi = bitcast<float>(d[p] & 0xFFFF0000u);
             }
-            vals[word_order_value(2 * p)] = (lo - bias) * s;
-            vals[word_order_value(2 * p + 1)] = (hi - bias) * s;
+            vals[word_order_value(2 * p)] = lo * s;
+            vals[word_order_value(2 * p + 1)] = hi * s;
         }
         float *o = static_cast<float *>(out) + (size_t)idx * 8;
 #pragma unroll

@@ -10,8 +10,9 @@
 //   * issues a batch of U independent loads per lane before any math on them,
 //     so U * 16 bytes per lane stay in flight,
 //   * keeps the zero-points packed and extracts the nibble in registers,
-//   * spends about two vector ALU operations per weight (packed binary16 or
-//     bfloat16 dot products on unpacked pairs).
+//   * forms each weight's exact (q - z) in registers and multiplies it with
+//     packed binary16 or bfloat16 dot products, so every product is exact
+//     and the sums round only at the size of their own terms.
 //
 // Work decomposition.  A wavefront owns RO row octets (an octet is 8
 // consecutive rows, the rows that share one packed zero-point word) and one
@@ -22,9 +23,8 @@
 // chunk are read from LDS once for all RO rows of the lane.  One chunk is one 16-byte load (four words, 32 codes) and
 // lies inside a single quantization group for every g in {32, 64, 128}.
 //
-// Prologue.  The workgroup stages X (in word order, see wob_device.hpp), the
-// chunk sums of X, and the scales and packed zero-point words of its rows in
-// LDS with a few coalesced 16-byte loads per thread.  Each wave issues its
+// Prologue.  The workgroup stages X (in word order, see wob_device.hpp) and
+// the scales and packed zero-point words of its rows in LDS with a few coalesced 16-byte loads per thread.  Each wave issues its
 // first batch of weight loads before it waits for the staging loads, so the
 // prologue latency hides behind weight traffic.  The per-chunk metadata then
 // costs two LDS reads instead of two small global loads.  With K split over
@@ -35,14 +35,27 @@
 // workgroups share a CU instead of two (LDS), so the grid of 672 workgroups
 // runs in one generation (21.1 -> 16.8 us measured).
 //
-// Arithmetic: each word is unpacked with byte permutes into four pairs of
-// biased 16-bit numbers (B + q), B = 1024 for binary16 and 128 for bfloat16,
-// which are exact, and fed to v_dot2_f32_f16 / v_dot2_f32_bf16 with the
-// activation pairs.  Per chunk, sum_k (q_k - z) x_k = sum_k (B + q_k) x_k -
-// (B + z) * sum_k x_k; the chunk result is scaled once.  Products are exact in
-// fp32 and accumulation is fp32; the bias term adds a rounding error of order
-// 2^-24 * B * sum|x| per chunk, far inside the parity tolerance.  About 1.5
-// vector operations per weight at M = 1.
+// Arithmetic: each word becomes four pairs of exact (q - z) values in the
+// activation dtype (binary16: byte permutes place each code under the
+// exponent byte of 1024 and one packed add of -(1024 + z) per pair removes
+// the bias; bfloat16: byte-to-float conversions, an fp32 subtract and a pack),
+// which v_dot2_f32_f16 / v_dot2_f32_bf16 multiply with the activation pairs.
+// |q - z| <= 15 has four significant bits, so every product is exact in fp32;
+// each chunk's sum of products sum_k (q_k - z) x_k is scaled once by its s.
+// The sums round only at the size of their own terms: weights that dequantize
+// to zero give exact zeros whatever the activations.  About 1.9 vector
+// operations per weight at M = 1 (binary16).
+//
+// Measured alternatives (MI355X, one box, decode 1 x 43008 x 5376): folding
+// the zero-point out of the sums as sum (B + q) x - (B + z) sum x with the
+// biased codes as operands costs 1.4 operations per weight (23.5 us against
+// 25.9 us) but rounds at B times the size of the terms: with B = 1024 (the
+// exponent-byte trick) weights that dequantize to zero under activations with
+// 1e3 outliers miss the parity bound 15-fold; B = 16 (codes shifted under the
+// exponent of 16) stays inside it at half the bound and runs slower (26.7 us:
+// its and-or pairs do not fuse); B = 0 (codes as binary16 subnormals) runs
+// into v_dot2c_f32_f16's reduced precision on subnormal operands (errors of
+// 2^-16 relative to the activations, against 2^-24 with normal operands).
 //
 // Weight loads stream through a ring of D chunk slots: computing chunk i frees
 // its slot, which immediately receives the load of chunk i + D.  One load is
@@ -74,13 +87,12 @@ constexpr int SK_ZR = 3; // zero-point words
 // LDS carve-up, in bytes, shared by the kernel and the host-side size check.
 // Scales are staged only when `sc_lds` (see the kernel's SG parameter).
 struct SkLds {
-    int x, xsum, sc, zp, red, total;
+    int x, sc, zp, red, total;
     __host__ __device__ SkLds(int M, int K, int G, int octs_per_wg, bool sc_lds)
     {
         const int RB = ((K + 255) >> 8) * 32; // 16-byte blocks per X row
         x = 0;
-        xsum = x + M * RB * 16;
-        sc = xsum + M * (K >> 5) * 4;
+        sc = x + M * RB * 16;
         zp = sc + (sc_lds ? ((octs_per_wg * 8 * G * 2 + 15) & ~15) : 0);
         red = zp + ((octs_per_wg * G * 4 + 15) & ~15);
         total = red + SK_MAX_WAVES * 2 * M * 8 * 4; // up to two octets per wave
@@ -111,7 +123,6 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
     const int octs_per_wg = (nthr >> 6) / ksplit * RO;
     const SkLds L(M, K, G, octs_per_wg, !SG);
     u32x4 *xl = reinterpret_cast<u32x4 *>(smem + L.x);
-    float *xsum = reinterpret_cast<float *>(smem + L.xsum);
     uint16_t *sl = reinterpret_cast<uint16_t *>(smem + L.sc);
     uint32_t *zl = reinterpret_cast<uint32_t *>(smem + L.zp);
     float *red = reinterpret_cast<float *>(smem + L.red);
@@ -185,31 +196,16 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
         load_chunk(ring[d], sring[d], min(d, max(n_it - 1, 0)));
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- stage X (word order, conflict-free block layout) and chunk sums ----
+    // ---- stage X (word order, conflict-free block layout) ----
     const int rowblk = K >> 3;
 #pragma unroll
     for (int t = 0; t < SK_XR; ++t) {
         const int i = tid + nthr * t;
-        float bs = 0.f; // sum of this block's 8 values
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if constexpr (DT == DT_F16)
-                bs = __builtin_amdgcn_fdot2(bitcast<half2_t>(xr[t][e]),
-                                            half2_t{(_Float16)1.f, (_Float16)1.f}, bs, false);
-            else
-                bs = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(xr[t][e]),
-                                                     bitcast<bf162_t>(0x3F803F80u), bs, false);
-        }
-        // the four blocks of a chunk sit in four consecutive lanes
-        bs += __shfl_xor(bs, 1);
-        bs += __shfl_xor(bs, 2);
         if (i < nvec) {
             const int m = i / rowblk;
             const int tb = i - m * rowblk;
             const int j = tb >> 2, wi = tb & 3;
             xl[m * RB + (j >> 3) * 32 + wi * 8 + (j & 7)] = to_word_order(xr[t]);
-            if (wi == 0)
-                xsum[m * C + j] = bs;
         }
     }
     {
@@ -234,8 +230,6 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
     // Large M * K (long rows): whatever did not fit the prologue registers,
     // SK_XR loads per thread at a time so their latencies overlap (one load
     // per iteration serialized a dozen L2 round trips on 1 x 21504 rows).
-    // nvec and the thread offsets of a 4-lane group are multiples of 4, so
-    // the lanes of a chunk's group enter and leave the loop together.
     for (int i0 = tid + nthr * SK_XR; i0 < nvec; i0 += nthr * SK_XR) {
         u32x4 v[SK_XR];
 #pragma unroll
@@ -244,25 +238,11 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
 #pragma unroll
         for (int t = 0; t < SK_XR; ++t) {
             const int i = i0 + nthr * t;
-            float bs = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if constexpr (DT == DT_F16)
-                    bs = __builtin_amdgcn_fdot2(bitcast<half2_t>(v[t][e]),
-                                                half2_t{(_Float16)1.f, (_Float16)1.f}, bs, false);
-                else
-                    bs = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(v[t][e]),
-                                                         bitcast<bf162_t>(0x3F803F80u), bs, false);
-            }
-            bs += __shfl_xor(bs, 1);
-            bs += __shfl_xor(bs, 2);
             if (i < nvec) {
                 const int m = i / rowblk;
                 const int tb = i - m * rowblk;
                 const int j = tb >> 2, wi = tb & 3;
                 xl[m * RB + (j >> 3) * 32 + wi * 8 + (j & 7)] = to_word_order(v[t]);
-                if (wi == 0)
-                    xsum[m * C + j] = bs;
             }
         }
     }
@@ -276,9 +256,6 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
     }
     __syncthreads();
 
-    constexpr uint32_t MAGIC = DT == DT_F16 ? MAGIC4_F16 : MAGIC4_BF16;
-    constexpr float BIAS = DT == DT_F16 ? 1024.f : 128.f;
-
     float acc[RO][M];
 #pragma unroll
     for (int o = 0; o < RO; ++o)
@@ -291,23 +268,29 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
     if (n_it > 0) {
         // this lane's LDS data: X blocks of chunk jf + 8 i, word wi at 32 i + 8 wi
         const u32x4 *xb0 = xl + (jf >> 3) * 32 + (jf & 7);
-        const float *xs0 = xsum + jf;
         const uint16_t *sp = sl + (woct * 8 + r) * G + (jf >> GS); // octet o: + 8 G o
         const uint32_t *zp = zl + woct * G + (jf >> GS);            // octet o: + G o
 
         auto chunk = [&](int i, const u32x4(&wv)[RO], const uint32_t(&sv)[RO]) {
-            // unpack every row's word pairs first; then, per activation row,
-            // read that row's X blocks once and use them for all RO rows
+            // unpack every row's (q - z) pairs first; then, per activation
+            // row, read that row's X blocks once and use them for all RO rows
             u32x4 pr[RO][4];
-            float sc[RO], bias[RO];
+            float sc[RO];
 #pragma unroll
             for (int o = 0; o < RO; ++o) {
                 sc[o] = act_to_f32<DT>(SG ? (uint16_t)sv[o] : sp[8 * G * o + SU * i]);
                 const uint32_t z = HAS_Z ? nib(zp[G * o + SU * i], r) : 8u;
-                bias[o] = BIAS + (float)z;
+                if constexpr (DT == DT_F16) {
+                    const uint32_t nb2 = f16_neg_bias2(z);
 #pragma unroll
-                for (int wi = 0; wi < 4; ++wi)
-                    pr[o][wi] = nib_pairs_biased(wv[o][wi], MAGIC);
+                    for (int wi = 0; wi < 4; ++wi)
+                        pr[o][wi] = w4_diff_pairs_f16(wv[o][wi], nb2);
+                } else {
+                    const float zf = (float)z;
+#pragma unroll
+                    for (int wi = 0; wi < 4; ++wi)
+                        pr[o][wi] = w4_diff_pairs_bf16(wv[o][wi], zf);
+                }
             }
 #pragma unroll
             for (int m = 0; m < M; ++m) {
@@ -315,7 +298,6 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
 #pragma unroll
                 for (int wi = 0; wi < 4; ++wi)
                     xv[wi] = xb0[m * RB + 32 * i + 8 * wi];
-                const float xsv = xs0[m * C + 8 * i];
 #pragma unroll
                 for (int o = 0; o < RO; ++o) {
                     float a0 = 0.f, a1 = 0.f;
@@ -334,8 +316,7 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
                             a1 = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(pr[o][wi][3]), bitcast<bf162_t>(x4[3]), a1, false);
                         }
                     }
-                    const float t = fmaf(-bias[o], xsv, a0 + a1);
-                    acc[o][m] = fmaf(sc[o], t, acc[o][m]);
+                    acc[o][m] = fmaf(sc[o], a0 + a1, acc[o][m]);
                 }
             }
         };

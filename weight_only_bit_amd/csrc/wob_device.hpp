@@ -5,14 +5,13 @@
 // instead of expanding to 2 bytes", section Change; the weight words use the
 // same rule along K): value i of a packed word sits in bits 4*i.
 //
-// Element order inside a word.  Shifting a word right by 4p and masking with
-// 0x000F000F leaves value p in the low half and value p+4 in the high half.
-// OR-ing 0x6400 (binary16 1024.0) into each half turns them into the exact
-// binary16 numbers 1024+q, and subtracting 1024+z gives q-z exactly.  A word
-// therefore dequantizes into four half pairs holding values
+// Element order inside a word (skinny GEMV form).  Masking a word with
+// 0x0F0F0F0F leaves values 0, 2, 4, 6 in its four bytes, and shifting it right
+// by 4 first leaves values 1, 3, 5, 7.  Pairing byte b with byte b + 2 of
+// either gives 16-bit pairs holding values
 //     (0,4) (1,5) (2,6) (3,7)
-// so every consumer stores the matching activations in that same order
-// ("word order" below).  A dot product is invariant under a common
+// so every consumer of that form stores the matching activations in that same
+// order ("word order" below).  A dot product is invariant under a common
 // permutation of both operands, so the order never changes a result.
 #pragma once
 
@@ -54,28 +53,62 @@ __device__ __forceinline__ u32x4 to_word_order(u32x4 v)
 }
 
 // ---------------------------------------------------------------------------
-// 4-bit unpack
+// 4-bit unpack into exact (q - z) pairs (the skinny GEMV's weight operand),
+// word order
 // ---------------------------------------------------------------------------
 
-// High byte of the biased 16-bit numbers: 0x64 gives binary16 1024 + q,
-// 0x43 gives bfloat16 128 + q (q < 16 sits in the low mantissa bits).
+// binary16 exponent byte of 1024: 0x64 in the high byte and a code q < 16 in
+// the low byte read as the exact binary16 number 1024 + q.
 constexpr uint32_t MAGIC4_F16 = 0x64646464u;
-constexpr uint32_t MAGIC4_BF16 = 0x43434343u;
 
-// All four biased pairs of a word, in word order, with byte permutes: after
-// masking, the even values sit in the bytes of t0 and the odd ones in t1, and
-// v_perm_b32 interleaves two of those bytes with two magic bytes.  Seven
-// vector operations per word.
-__device__ __forceinline__ u32x4 nib_pairs_biased(uint32_t w, uint32_t magic4)
+// binary16 pair -(1024 + z), -(1024 + z): adding it to a biased pair (1024 +
+// q_a, 1024 + q_b) leaves (q_a - z, q_b - z) exactly.
+__device__ __forceinline__ uint32_t f16_neg_bias2(uint32_t z)
 {
-    const uint32_t t0 = w & 0x0F0F0F0Fu;        // values 0, 2, 4, 6 in bytes 0..3
-    const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu; // values 1, 3, 5, 7
+    const uint32_t h = 0xE400u | z;
+    return h | (h << 16);
+}
+
+// The four (q - z) pairs of a word in word order, as binary16: after masking,
+// the even codes sit in the bytes of t0 and the odd ones in t1; v_perm_b32
+// interleaves two of those bytes with the exponent byte 0x64 (exact 1024 + q)
+// and one packed add of -(1024 + z) per pair removes the bias exactly.
+// Eleven vector operations per word.
+__device__ __forceinline__ u32x4 w4_diff_pairs_f16(uint32_t w, uint32_t negb2)
+{
+    const uint32_t t0 = w & 0x0F0F0F0Fu;        // codes 0, 2, 4, 6 in bytes 0..3
+    const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu; // codes 1, 3, 5, 7
+    const half2_t nb = bitcast<half2_t>(negb2);
     u32x4 o;
     // selector bytes 0-3 pick from t (src1), 4 picks the magic byte (src0)
-    o[0] = __builtin_amdgcn_perm(magic4, t0, 0x04020400u); // (v0, v4)
-    o[1] = __builtin_amdgcn_perm(magic4, t1, 0x04020400u); // (v1, v5)
-    o[2] = __builtin_amdgcn_perm(magic4, t0, 0x04030401u); // (v2, v6)
-    o[3] = __builtin_amdgcn_perm(magic4, t1, 0x04030401u); // (v3, v7)
+    o[0] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t0, 0x04020400u)) + nb); // (v0, v4)
+    o[1] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t1, 0x04020400u)) + nb); // (v1, v5)
+    o[2] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t0, 0x04030401u)) + nb); // (v2, v6)
+    o[3] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t1, 0x04030401u)) + nb); // (v3, v7)
+    return o;
+}
+
+// Two fp32 values -> one dword of two bfloat16 (nearest even; exact for the
+// small integers used here).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    return bitcast<uint32_t>(__builtin_convertvector(f2_t{a, b}, bf162_t));
+}
+
+// The four (q - z) pairs of a word in word order, as bfloat16: each code byte
+// becomes an fp32 integer, z is subtracted exactly, and each pair is packed
+// to bfloat16 (|q - z| <= 15 is exact there).  gfx950 has no packed bfloat16
+// add, so this goes through fp32.
+__device__ __forceinline__ u32x4 w4_diff_pairs_bf16(uint32_t w, float zf)
+{
+    const uint32_t t0 = w & 0x0F0F0F0Fu;        // codes 0, 2, 4, 6 in bytes 0..3
+    const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu; // codes 1, 3, 5, 7
+    u32x4 o;
+    o[0] = pack_bf16x2((float)(t0 & 0xFFu) - zf, (float)((t0 >> 16) & 0xFFu) - zf); // (v0, v4)
+    o[1] = pack_bf16x2((float)(t1 & 0xFFu) - zf, (float)((t1 >> 16) & 0xFFu) - zf); // (v1, v5)
+    o[2] = pack_bf16x2((float)((t0 >> 8) & 0xFFu) - zf, (float)(t0 >> 24) - zf);    // (v2, v6)
+    o[3] = pack_bf16x2((float)((t1 >> 8) & 0xFFu) - zf, (float)(t1 >> 24) - zf);    // (v3, v7)
     return o;
 }
 
@@ -187,7 +220,18 @@ __device__ __forceinline__ u32x4 w4_word_act8(uint32_t w, uint32_t sbits, uint32
 // becomes that scale by being placed in the binary32 exponent field ("Add
 // BF16xFP4 MoE GEMM stage1 kernel", Technical Details).  Output pairs are in
 // natural order: (0,1) (2,3) (4,5) (6,7).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t b) { return bitcast<float>(b << 23); }
+//
+// The byte-in-exponent placement is exact for b = 1..254.  The two ends of the
+// E8M0 range follow the OCP MX definition instead: b = 0 is 2^-127, which
+// binary32 holds as a subnormal (the shifted byte would read +0), and b = 255
+// is NaN (the shifted byte would read +Inf).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b)
+{
+    uint32_t bits = b << 23;
+    bits = b == 0u ? 0x00400000u : bits;   // 2^-127
+    bits = b == 255u ? 0x7FC00000u : bits; // NaN
+    return bitcast<float>(bits);
+}
 
 __device__ __forceinline__ u32x4 fp4_word_bf16x8(uint32_t w, float scale)
 {

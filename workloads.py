@@ -94,18 +94,51 @@ def w4a16_inputs(M, N, K, g, dtype, seed=0, symmetric=False, signed_scales=False
     rng = np.random.default_rng(seed)
     x = to_act_bits(rng.standard_normal((M, K), dtype=np.float32), dtype)
     qweight = _uniform_words(rng, (N, K // 8))
-    if signed_scales:
-        mag = 10.0 ** rng.uniform(-3.0, -1.0, size=(N, G))
-        sign = np.where(rng.integers(0, 2, size=(N, G)) == 1, -1.0, 1.0)
-        scales = to_act_bits((mag * sign).astype(np.float32), dtype)
-    else:
-        scales = to_act_bits(rng.uniform(1e-3, 2e-2, size=(N, G)).astype(np.float32), dtype)
+    scales = _scales(rng, (N, G), dtype, signed_scales)
     qzeros = None if symmetric else _uniform_words(rng, (N // 8, G))
     return dict(x=x, qweight=qweight, scales=scales, qzeros=qzeros,
                 M=M, N=N, K=K, g=g, dtype=dtype)
 
 
-def w4a16_grouped_inputs(group_rows, N, K, g, dtype, seed=0):
+def _scales(rng, shape, dtype, signed):
+    if signed:
+        mag = 10.0 ** rng.uniform(-3.0, -1.0, size=shape)
+        sign = np.where(rng.integers(0, 2, size=shape) == 1, -1.0, 1.0)
+        return to_act_bits((mag * sign).astype(np.float32), dtype)
+    return to_act_bits(rng.uniform(1e-3, 2e-2, size=shape).astype(np.float32), dtype)
+
+
+def w4a16_degenerate_inputs(M, N, K, g, dtype, seed=0, live_groups=0.1, outlier_cols=0.02,
+                            symmetric=False):
+    """Weights that mostly dequantize to zero under activations with outliers.
+
+    Every (row, group) draws a zero-point z uniform 0..15 (8 when symmetric);
+    the group's codes all equal z, except in a fraction ``live_groups`` of the
+    (row, group) pairs whose codes are uniform 0..15.  X ~ N(0,1), with a
+    fraction ``outlier_cols`` of the K columns scaled by +-U[100, 1000].
+    ``live_groups=0`` gives a matrix that dequantizes to all zeros.  Scales as
+    in w4a16_inputs.  Draw order: zero-points, live mask, live codes, X,
+    outlier columns, outlier factors, scales."""
+    assert K % g == 0 and N % 8 == 0
+    G = K // g
+    rng = np.random.default_rng(seed)
+    zeros = np.full((N, G), 8, np.int64) if symmetric else rng.integers(0, 16, (N, G))
+    live = rng.random((N, G)) < live_groups
+    codes = np.repeat(zeros, g, axis=1)
+    rand = rng.integers(0, 16, (N, K))
+    codes = np.where(np.repeat(live, g, axis=1), rand, codes)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    cols = rng.choice(K, max(1, int(K * outlier_cols)), replace=False)
+    fac = rng.uniform(100.0, 1000.0, cols.size) * np.where(rng.integers(0, 2, cols.size) == 1, -1, 1)
+    x[:, cols] *= fac.astype(np.float32)
+    scales = to_act_bits(rng.uniform(1e-3, 2e-2, size=(N, G)).astype(np.float32), dtype)
+    return dict(x=to_act_bits(x, dtype), qweight=pack_u4_along_k(codes), scales=scales,
+                qzeros=None if symmetric else pack_u4_along_n(zeros), M=M, N=N, K=K, g=g,
+                dtype=dtype)
+
+
+def w4a16_grouped_inputs(group_rows, N, K, g, dtype, seed=0, symmetric=False,
+                         signed_scales=False):
     """Ragged grouped operands: group e has group_rows[e] rows and its own weights."""
     E = len(group_rows)
     G = K // g
@@ -115,8 +148,8 @@ def w4a16_grouped_inputs(group_rows, N, K, g, dtype, seed=0):
     total = int(offsets[-1])
     x = to_act_bits(rng.standard_normal((total, K), dtype=np.float32), dtype)
     qweight = _uniform_words(rng, (E, N, K // 8))
-    scales = to_act_bits(rng.uniform(1e-3, 2e-2, size=(E, N, G)).astype(np.float32), dtype)
-    qzeros = _uniform_words(rng, (E, N // 8, G))
+    scales = _scales(rng, (E, N, G), dtype, signed_scales)
+    qzeros = None if symmetric else _uniform_words(rng, (E, N // 8, G))
     return dict(x=x, m_offsets=offsets, qweight=qweight, scales=scales, qzeros=qzeros,
                 N=N, K=K, g=g, dtype=dtype)
 
