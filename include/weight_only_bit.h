@@ -183,6 +183,24 @@ int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
                    int64_t K, int act, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mxfp4_moe_gemm without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the routing scratch lives in a static
+ * device array of 1 MiB (one per GPU, held until the process ends).  Same
+ * operands, rules, kernels and results as mxfp4_moe_gemm; additionally
+ * mxfp4_moe_gemm_workspace_size(T, topk, E, N, K) must not exceed 1 MiB
+ * (about 250,000 routed pairs T*topk at E = 32), else WOB_INVALID_ARG before
+ * any device call.  Every call on one GPU uses that GPU's one array, so calls
+ * that overlap on one GPU (concurrent streams or threads) race; calls ordered
+ * on one stream do not.  The array needs no clearing: each call rewrites what
+ * it reads.  Allocates nothing (no hipMalloc, hipFree or allocating library
+ * call); the array's device address is looked up once per device.
+ */
+int mxfp4_moe_gemm_noalloc(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
+                           const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E,
+                           int64_t N, int64_t K, int act, void *stream);
+
+/*
  * Dequantization probes: write out the weights as the GEMM kernels form them,
  * through the same device helpers, so the unpack / dequantize stage can be
  * compared bit for bit with its definition.  Source: zero-point page above,

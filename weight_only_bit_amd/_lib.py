@@ -20,7 +20,7 @@ ACT_NONE, ACT_SILU_MUL = 0, 1
 EXPORTS = [
     "wob_status_str", "wob_last_error", "wob_device_check",
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_grouped",
-    "mxfp4_moe_gemm_workspace_size", "mxfp4_moe_gemm",
+    "mxfp4_moe_gemm_workspace_size", "mxfp4_moe_gemm", "mxfp4_moe_gemm_noalloc",
     "w4a16_dequant", "mxfp4_dequant", "wob_stream_read",
 ]
 
@@ -40,6 +40,8 @@ _SIGNATURES = {
     "mxfp4_moe_gemm_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "mxfp4_moe_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i, _vp, _sz,
                             _vp]),
+    "mxfp4_moe_gemm_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i,
+                                    _vp]),
     "w4a16_dequant": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _i64, _i64, _i64, _vp]),
     "mxfp4_dequant": (_i, [_vp, _vp, _vp, _i64, _i64, _vp]),
     "wob_stream_read": (_i, [_vp, _sz, _vp, _vp]),

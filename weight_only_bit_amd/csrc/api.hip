@@ -292,6 +292,35 @@ int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
                     "mxfp4 moe");
 }
 
+int mxfp4_moe_gemm_noalloc(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
+                           const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E,
+                           int64_t N, int64_t K, int act, void *stream)
+{
+    bool noop;
+    int s = check_moe(x, topk_ids, w_fp4, w_scale, y, T, topk, E, N, K, act, &noop);
+    if (s != WOB_OK)
+        return s;
+    if (noop)
+        return ok();
+    const size_t need = wob::moe_workspace_bytes(T, topk, E);
+    if (need > wob::moe_scratch_bytes())
+        return fail(WOB_INVALID_ARG,
+                    "routing scratch of %zu bytes (T*topk=%lld pairs, E=%lld) exceeds the "
+                    "%zu-byte static scratch of the allocation-free entry point",
+                    need, (long long)(T * topk), (long long)E, wob::moe_scratch_bytes());
+    s = arch_gate();
+    if (s != WOB_OK)
+        return s;
+    void *scratch = nullptr;
+    const hipError_t e = wob::moe_scratch(&scratch);
+    if (e != hipSuccess)
+        return fail(WOB_HIP, "static scratch lookup: %s", hipGetErrorString(e));
+    return launched(wob::launch_mxfp4_moe(x, topk_ids, w_fp4, w_scale, y, (int)T, (int)topk,
+                                          (int)E, (int)N, (int)K, act, scratch,
+                                          static_cast<hipStream_t>(stream)),
+                    "mxfp4 moe (static scratch)");
+}
+
 int w4a16_dequant(const int32_t *qweight, const void *scales, int scales_dtype,
                   const void *qzeros, int zeros_dtype, void *out, int out_dtype, int64_t N,
                   int64_t K, int64_t group_size, void *stream)

@@ -32,6 +32,11 @@
 
 #include <algorithm>
 
+// Static routing scratch of the allocation-free entry point (see
+// moe_scratch below); file scope, one copy per device.
+static constexpr size_t MOE_SCRATCH_BYTES = (size_t)1 << 20;
+static __device__ __align__(256) uint8_t moe_static_scratch[MOE_SCRATCH_BYTES];
+
 namespace wob {
 namespace {
 
@@ -537,6 +542,39 @@ hipError_t launch_gemm(const void *x, const uint8_t *w_fp4, const uint8_t *w_sca
 }
 
 } // namespace
+
+// ---- Allocation-free form: routing scratch in a static device array -------
+
+// One copy per GPU the library runs on, kept until the process ends; its
+// device address is looked up once per device (below).  Every call on a GPU
+// shares it: the routing kernel rewrites everything the GEMM reads from it
+// (tile count, tile table, sorted pairs) before the GEMM runs, so nothing has
+// to be cleared, but calls that overlap on one GPU race.
+size_t moe_scratch_bytes() { return MOE_SCRATCH_BYTES; }
+
+hipError_t moe_scratch(void **ptr)
+{
+    static std::atomic<void *> dev_ptr[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= 64)
+        return hipErrorInvalidDevice;
+    void *p = dev_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // with `dev` current: this device's copy of the array (the array's
+        // name in host code is only a stand-in, not a device address)
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(moe_static_scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!p || (reinterpret_cast<uintptr_t>(p) & 255u) != 0)
+            return hipErrorInvalidSymbol;
+        dev_ptr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t E)
 {

@@ -51,6 +51,10 @@ hipError_t launch_w4a16_grouped(const W4Args &a, const int64_t *m_offsets, int n
 
 // MoE stage 1, BF16 x MXFP4.
 size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+// The static routing scratch of the allocation-free entry point: its size,
+// and its address on the current device (looked up on first use per device).
+size_t moe_scratch_bytes();
+hipError_t moe_scratch(void **ptr);
 hipError_t launch_mxfp4_moe(const void *x, const int32_t *ids, const uint8_t *w_fp4,
                             const uint8_t *w_scale, void *y, int T, int topk, int E, int N, int K,
                             int act, void *workspace, hipStream_t stream);
