@@ -17,7 +17,9 @@ distance holds for every step, the first of a replay included.
 Timed region.  W untimed eager warm-up steps; then the K steps of a replay
 are captured in HIP graphs (graph j holds the K steps that start at copy
 j*K mod n; n / gcd(n, K) graphs close the cycle) and every graph is replayed
-once untimed (the first replay uploads it).  Then R replays (default 5) of K
+once untimed (the first replay uploads it), then in whole cycles for 0.3 s
+(untimed: the clocks ramp after an idle period, and the first replays ran up
+to a quarter slower).  Then R replays (default 5) of K
 steps each are timed one by one, each bracketed by torch.cuda.synchronize(),
 with HIP events recorded on the stream the kernels run on.  The step time is
 the median over the R replays of elapsed / K (the minimum is reported
@@ -65,6 +67,7 @@ MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA, published
 MALL_BYTES = 256 << 20         # Infinity Cache
 REUSE_BYTES = 2 * MALL_BYTES   # bytes touched between two uses of one operand copy
 MAX_COPIES = 512               # tiny calls: the cache cannot be defeated; labelled hot
+SETTLE_S = 0.3                 # untimed replays before each timed series (clock ramp)
 FETCH_FACTOR_DEFAULT = 2.0     # FETCH_SIZE reads half of a device copy's bytes on this part
 TRAFFIC_SOURCE = ("committed rocprofv3 counters (profiles/traffic.json: FETCH_SIZE x fetch "
                   "factor + WRITE_SIZE per dispatch); null when the kernel sources changed "
@@ -184,6 +187,13 @@ def time_steps(step, steps: int, warmup: int, copies: int, reps: int) -> Timing:
     for g in graphs:  # untimed: the first replay of a graph uploads it
         g.replay()
     torch.cuda.synchronize()
+    # untimed: whole cycles until the clocks have settled (the first replays
+    # after an idle period run up to a quarter slower while they ramp)
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     reps_ms = []
     for r in range(reps):

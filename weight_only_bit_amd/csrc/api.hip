@@ -135,6 +135,30 @@ wob::W4Args make_args(const void *x, int dt, const int32_t *qweight, const void 
 
 } // namespace
 
+namespace wob {
+
+DevTopo device_topology()
+{
+    static std::atomic<uint64_t> cache[64]; // cus << 32 | xcds, 0 = not queried
+    constexpr DevTopo fallback{256, 8};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fallback;
+    uint64_t v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0, xcds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess ||
+            cus <= 0 || xcds <= 0)
+            return fallback;
+        v = ((uint64_t)cus << 32) | (uint32_t)xcds;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return DevTopo{(int)(v >> 32), (int)(uint32_t)v};
+}
+
+} // namespace wob
+
 extern "C" {
 
 const char *wob_status_str(int status)

@@ -47,8 +47,13 @@ namespace {
 // rows) for the fused gate / up activation, which pairs weight blocks.
 template <bool ACT>
 constexpr int moe_nb() { return ACT ? 2 : 3; }
+// 32-row activation blocks per expert tile, at most: the fused-activation
+// tile stops at 7 (224 rows), since its 8-block form (the full 256 fp32
+// accumulator registers) spilled a register; a larger expert takes two tiles.
 template <bool ACT>
-constexpr int moe_tm() { return TileGeo<moe_nb<ACT>()>::TM_MAX; } // rows per expert tile
+constexpr int moe_mb_max() { return ACT ? 7 : TileGeo<moe_nb<ACT>()>::MB_MAX; }
+template <bool ACT>
+constexpr int moe_tm() { return 32 * moe_mb_max<ACT>(); } // rows per expert tile
 template <bool ACT>
 constexpr int moe_tn() { return TileGeo<moe_nb<ACT>()>::TN; } // weight rows per tile
 constexpr int MOE_TM_MIN = moe_tm<false>() < moe_tm<true>() ? moe_tm<false>() : moe_tm<true>();
@@ -214,12 +219,12 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w_fp4,
     const uint8_t *__restrict__ w_scale, uint16_t *__restrict__ y, const int32_t *__restrict__ hdr,
     const int4 *__restrict__ tiles, const int32_t *__restrict__ sorted, int topk, int E, int N,
-    int K, int n_nt)
+    int K, int n_nt, int nxcd)
 {
     constexpr int NB = moe_nb<ACT>();
     constexpr int TW = ACT ? moe_tn<ACT>() / 2 : moe_tn<ACT>(); // output columns per tile
     extern __shared__ __align__(16) uint8_t smem[];
-    const int t = xcd_tile(hdr[0] * n_nt);
+    const int t = xcd_tile(hdr[0] * n_nt, nxcd);
     if (t < 0)
         return;
     const int i = t / n_nt;
@@ -235,8 +240,8 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
     const TileLane tl;
     const FmtFP4<ACT, NB> fmt(w_fp4 + (size_t)e * N * (K >> 1),
                                   w_scale + (size_t)e * N * (K >> 5), N, K, n0, tl);
-    moe_dispatch<ACT, TileGeo<NB>::MB_MAX>((rows + 31) >> 5, fmt, pairs, rows, topk, x, y, K,
-                                               N, n0, smem, tl);
+    moe_dispatch<ACT, moe_mb_max<ACT>()>((rows + 31) >> 5, fmt, pairs, rows, topk, x, y, K, N,
+                                         n0, smem, tl);
 }
 
 // ---- Decode path: at most MG_TOKENS tokens --------------------------------
@@ -532,12 +537,13 @@ hipError_t launch_gemm(const void *x, const uint8_t *w_fp4, const uint8_t *w_sca
     const int tw = ACT ? moe_tn<ACT>() / 2 : moe_tn<ACT>();
     const int nout = ACT ? N / 2 : N;
     const int n_nt = (nout + tw - 1) / tw;
-    const int64_t grid = 8 * (((int64_t)max_tiles(P, E) * n_nt + 7) / 8);
+    const int nxcd = device_topology().xcds;
+    const int64_t grid = (int64_t)nxcd * (((int64_t)max_tiles(P, E) * n_nt + nxcd - 1) / nxcd);
     if (grid > INT32_MAX)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(TL_THREADS), (size_t)LDS, stream,
                        static_cast<const uint16_t *>(x), w_fp4, w_scale, static_cast<uint16_t *>(y),
-                       w.hdr, w.tiles, w.sorted, topk, E, N, K, n_nt);
+                       w.hdr, w.tiles, w.sorted, topk, E, N, K, n_nt, nxcd);
     return hipGetLastError();
 }
 

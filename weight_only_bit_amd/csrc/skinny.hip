@@ -415,10 +415,8 @@ struct SkCfg {
     int ro, waves, ksplit;
 };
 
-// Compute units of gfx950 (8 XCDs x 32): workgroups are spread over them.
-constexpr int SK_CUS = 256;
-
-SkCfg sk_config(int M, int N, int K)
+// `cus`: compute units of the device (the workgroups are spread over them).
+SkCfg sk_config(int M, int N, int K, int cus)
 {
     const int octs = N / 8;
     const int C = K / 32;
@@ -427,15 +425,15 @@ SkCfg sk_config(int M, int N, int K)
     // the compute units (each CU streams at a bounded rate, so the CU with the
     // most workgroups sets the kernel time; measured on the decode shape, the
     // CUs holding one workgroup more than the others finished last).
-    if (octs >= 16 * SK_CUS) {
+    if (octs >= 16 * cus) {
         SkCfg best{1, SK_WAVES, 1};
         double best_eff = -1.0;
         for (int ro = 1; ro <= (M <= 2 ? 2 : 1); ++ro) {
             const int units = (octs + ro - 1) / ro;
             for (int w = SK_MAX_WAVES; w >= 2; --w) {
                 const int wgs = (units + w - 1) / w;
-                const int per_cu = (wgs + SK_CUS - 1) / SK_CUS;
-                const double eff = (double)octs / ((double)SK_CUS * per_cu * w * ro);
+                const int per_cu = (wgs + cus - 1) / cus;
+                const double eff = (double)octs / ((double)cus * per_cu * w * ro);
                 if (eff > best_eff + 1e-9) {
                     best_eff = eff;
                     best = SkCfg{ro, w, 1};
@@ -454,7 +452,7 @@ SkCfg sk_config(int M, int N, int K)
 
 int lds_bytes(int M, int N, int K, int g)
 {
-    const SkCfg c = sk_config(M, N, K);
+    const SkCfg c = sk_config(M, N, K, device_topology().cus);
     return SkLds(M, K, K / g, c.waves / c.ksplit * c.ro, c.ksplit == 1).total;
 }
 
@@ -494,7 +492,7 @@ hipError_t launch_g(const W4Args &a, const SkCfg &c, size_t lds, hipStream_t str
 template <int DT, int M>
 hipError_t launch_m(const W4Args &a, hipStream_t stream)
 {
-    const SkCfg c = sk_config(M, a.N, a.K);
+    const SkCfg c = sk_config(M, a.N, a.K, device_topology().cus);
     const size_t lds = (size_t)lds_bytes(M, a.N, a.K, a.g);
     switch (a.g) {
     case 32: return launch_g<DT, M, 0>(a, c, lds, stream);

@@ -71,8 +71,8 @@ __device__ __forceinline__ void group_range(const int64_t *off, int g, int total
 // Locate this workgroup's tile in the grouped problem.  Every wave runs the
 // same wave-uniform computation (no LDS, no barrier).  Returns false when
 // the workgroup has no tile.
-__device__ bool grouped_tile(const int64_t *off, int G, int total_M, int TM, int n_nt, int &e,
-                             int &m0, int &rows, int &nt)
+__device__ bool grouped_tile(const int64_t *off, int G, int total_M, int TM, int n_nt, int nxcd,
+                             int &e, int &m0, int &rows, int &nt)
 {
     const int lane = threadIdx.x & 63;
     int total = 0;
@@ -86,7 +86,7 @@ __device__ bool grouped_tile(const int64_t *off, int G, int total_M, int TM, int
         }
         total += wave_sum_dev(tiles);
     }
-    const int t = xcd_tile(total * n_nt);
+    const int t = xcd_tile(total * n_nt, nxcd);
     if (t < 0)
         return false;
     const int i = t / n_nt;
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros,
     uint16_t *__restrict__ y, const int64_t *__restrict__ m_offsets, int num_groups, int M, int N,
-    int K, int gshift, int n_mt, int n_nt)
+    int K, int gshift, int n_mt, int n_nt, int nxcd)
 {
     using GEO = TileGeo<NB>;
     constexpr int TMX = GEO::TM_MAX;
@@ -156,14 +156,14 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
 
     int e = 0, m0, rows, nt;
     if (!m_offsets) {
-        const int t = xcd_tile(n_mt * n_nt);
+        const int t = xcd_tile(n_mt * n_nt, nxcd);
         if (t < 0)
             return;
         const int mt = t / n_nt;
         nt = t - mt * n_nt;
         m0 = mt * TMX;
         rows = min(TMX, M - m0);
-    } else if (!grouped_tile(m_offsets, num_groups, M, TMX, n_nt, e, m0, rows, nt)) {
+    } else if (!grouped_tile(m_offsets, num_groups, M, TMX, n_nt, nxcd, e, m0, rows, nt)) {
         return;
     }
     if (rows <= 0)
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
 
 template <int DT, int NB, bool HAS_Z, bool GW>
 hipError_t launch_k(const W4Args &a, const int64_t *m_offsets, int num_groups, int grid, int n_mt,
-                    int n_nt, size_t lds, hipStream_t stream)
+                    int n_nt, int nxcd, size_t lds, hipStream_t stream)
 {
     const int gshift = a.g == 32 ? 0 : a.g == 64 ? 1 : 2;
     auto kern = w4a16_tiled_kernel<DT, NB, HAS_Z, GW>;
@@ -202,7 +202,7 @@ hipError_t launch_k(const W4Args &a, const int64_t *m_offsets, int num_groups, i
                        static_cast<const uint16_t *>(a.x), a.qweight,
                        static_cast<const uint16_t *>(a.scales), a.qzeros,
                        static_cast<uint16_t *>(a.y), m_offsets, num_groups, a.M, a.N, a.K, gshift,
-                       n_mt, n_nt);
+                       n_mt, n_nt, nxcd);
     return hipGetLastError();
 }
 
@@ -212,20 +212,21 @@ hipError_t launch_zg(const W4Args &a, const int64_t *m_offsets, int num_groups, 
     using GEO = TileGeo<TILED_NB>;
     constexpr int TMX = GEO::TM_MAX;
     const int n_nt = (a.N + GEO::TN - 1) / GEO::TN;
+    const int nxcd = device_topology().xcds;
     if (!m_offsets) {
         // One tile row when M fits in it: size LDS for the blocks it needs.
         const int n_mt = (a.M + TMX - 1) / TMX;
         const int mb = n_mt == 1 ? (a.M + 31) / 32 : GEO::MB_MAX;
-        const int grid = 8 * ((n_mt * n_nt + 7) / 8);
-        return launch_k<DT, TILED_NB, HAS_Z, GW>(a, nullptr, 0, grid, n_mt, n_nt,
+        const int grid = nxcd * ((n_mt * n_nt + nxcd - 1) / nxcd);
+        return launch_k<DT, TILED_NB, HAS_Z, GW>(a, nullptr, 0, grid, n_mt, n_nt, nxcd,
                                                  (size_t)GEO::lds_bytes(mb), stream);
     }
     // Upper bound on the tiles of all groups: sum of ceil(rows_e / TMX).
     const int64_t max_mt = (a.M + TMX - 1) / TMX + num_groups;
-    const int64_t grid = 8 * ((max_mt * n_nt + 7) / 8);
+    const int64_t grid = (int64_t)nxcd * ((max_mt * n_nt + nxcd - 1) / nxcd);
     if (grid > INT_MAX)
         return hipErrorInvalidValue;
-    return launch_k<DT, TILED_NB, HAS_Z, GW>(a, m_offsets, num_groups, (int)grid, 0, n_nt,
+    return launch_k<DT, TILED_NB, HAS_Z, GW>(a, m_offsets, num_groups, (int)grid, 0, n_nt, nxcd,
                                              (size_t)GEO::lds_bytes(GEO::MB_MAX), stream);
 }
 

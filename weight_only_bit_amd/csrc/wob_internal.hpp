@@ -28,6 +28,14 @@ inline hipError_t lds_optin(const void *kern, int bytes, std::atomic<uint64_t> &
     return e;
 }
 
+// Compute units and XCDs of the current device (the XCD count is the number
+// of L2 domains that workgroups are dealt to round-robin).  Queried once per
+// device; {256, 8} (MI355X) when the device cannot be queried.
+struct DevTopo {
+    int cus, xcds;
+};
+DevTopo device_topology();
+
 struct W4Args {
     const void *x;
     const uint32_t *qweight;

@@ -491,16 +491,19 @@ __device__ __forceinline__ void tile_store_zero(const YRows &yr, int rows, int n
     }
 }
 
-// XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD takes a
-// contiguous run of the `tiles` tiles (N fastest), so its workgroups share
-// activation rows in that XCD's L2.  Returns -1 for workgroups beyond the run.
-__device__ __forceinline__ int xcd_tile(int tiles)
+// XCD-aware tile order: workgroups are dealt to the device's `nxcd` XCDs
+// round-robin (workgroup b runs on XCD b % nxcd); each XCD takes a contiguous
+// run of the `tiles` tiles (N fastest), so its workgroups share activation
+// rows in that XCD's L2.  The grid holds nxcd * ceil(tiles / nxcd)
+// workgroups; returns -1 for those beyond the run.
+__device__ __forceinline__ int xcd_tile(int tiles, int nxcd)
 {
-    const int per_xcd = (tiles + 7) >> 3;
+    const int per_xcd = (tiles + nxcd - 1) / nxcd;
     const int b = blockIdx.x;
-    if ((b >> 3) >= per_xcd)
+    const int j = b / nxcd;
+    if (j >= per_xcd)
         return -1;
-    const int t = (b & 7) * per_xcd + (b >> 3);
+    const int t = (b - j * nxcd) * per_xcd + j;
     return t < tiles ? t : -1;
 }
 
