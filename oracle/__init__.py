@@ -239,6 +239,39 @@ def mxfp4_moe_gemm_sampled(x, ids, w_fp4, w_scale, topk, E, N, K, ts, slots, ns)
     return out
 
 
+def mxfp4_moe_stage2(a, ids, w, w2_fp4, w2_scale, T, topk, E, H, I):
+    """fp64 y[T][H] of MoE stage 2 (a [T][topk][I] bf16 bits, w [T][topk] fp32)."""
+    aa = _c(a, np.uint16)
+    ii = _c(ids, np.int32)
+    ww = _c(w, np.float32)
+    w2 = _c(w2_fp4, np.uint8)
+    s2 = _c(w2_scale, np.uint8)
+    scratch = np.empty(I, np.float32)
+    pre = np.empty(T * topk * H, np.float64)
+    y = np.empty((T, H), np.float64)
+    _load().oracle_mxfp4_moe_stage2(_p(aa), _p(ii), _p(ww), _p(w2), _p(s2), ctypes.c_int64(T),
+                                    ctypes.c_int64(topk), ctypes.c_int64(E), ctypes.c_int64(H),
+                                    ctypes.c_int64(I), _p(scratch), _p(pre), _p(y))
+    return y
+
+
+def mxfp4_moe_stage2_sampled(a, ids, w, w2_fp4, w2_scale, topk, E, H, I, ts, hs):
+    aa = _c(a, np.uint16)
+    ii = _c(ids, np.int32)
+    ww = _c(w, np.float32)
+    w2 = _c(w2_fp4, np.uint8)
+    s2 = _c(w2_scale, np.uint8)
+    ts = _c(ts, np.int64)
+    hs = _c(hs, np.int64)
+    scratch = np.empty(I, np.float32)
+    out = np.empty(ts.shape, np.float64)
+    _load().oracle_mxfp4_moe_stage2_sampled(_p(aa), _p(ii), _p(ww), _p(w2), _p(s2),
+                                            ctypes.c_int64(topk), ctypes.c_int64(E),
+                                            ctypes.c_int64(H), ctypes.c_int64(I), _p(ts), _p(hs),
+                                            ctypes.c_int64(ts.size), _p(scratch), _p(out))
+    return out
+
+
 def tolerance_ok(y_test, y_ref):
     """The parity rule: |y - y_ref| <= 1e-3 + 1e-2 * max|y_ref| elementwise, no NaN/Inf.
 

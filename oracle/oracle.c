@@ -34,7 +34,10 @@
  *  - MXFP4 bytes hold the even-k element in the low nibble;
  *  - an expert id outside [0, E) yields an all-zero output row;
  *  - the stage-1 activation is silu(gate) * up, silu(v) = v / (1 + e^-v),
- *    with gate the first N/2 outputs of a row and up the last N/2.
+ *    with gate the first N/2 outputs of a row and up the last N/2;
+ *  - stage 2 (not defined on the pages) is the down projection of the
+ *    stage-1 activation rows with each expert's W2, weighted by the routing
+ *    weight and summed over the token's slots.
  *
  * Parity pins (tests/test_oracle_*.py): brute-force integer matmul, nibble
  * pack/unpack round trip with hand words, dense fp64/fp32 GEMM on the oracle's
@@ -391,4 +394,68 @@ void oracle_silu_mul(const double *ypre, int64_t rows, int64_t N, double *out)
             double u = ypre[r * N + I + n];
             out[r * I + n] = g / (1.0 + exp(-g)) * u;
         }
+}
+
+/*
+ * MoE stage 2 (reading; the stage-1 page names its kernel "stage1" and W1's
+ * gate / up halves but does not define the second stage): the down
+ * projection of each routed row of the stage-1 activation output, weighted by
+ * its routing weight and summed over the token's slots,
+ *   y[t][h] = sum over s < topk with e = ids[t][s] in [0, E) of
+ *             w[t][s] * sum_i a[t][s][i] * w2_e[h][i]
+ * a [T][topk][I] bfloat16; w [T][topk] binary32 routing weights;
+ * w2_fp4 [E][H][I/2] and w2_scale [E][H][I/32] as in stage 1 (MXFP4).
+ * Slots whose id lies outside [0, E) contribute nothing.  Each slot's dot
+ * product is accumulated in binary64 (i ascending), then the weighted slots
+ * are summed in slot order.  pre is caller scratch of T*topk*H doubles.
+ */
+void oracle_mxfp4_moe_stage2(const uint16_t *a, const int32_t *ids, const float *w,
+                             const uint8_t *w2_fp4, const uint8_t *w2_scale, int64_t T,
+                             int64_t topk, int64_t E, int64_t H, int64_t I, float *w_row,
+                             double *pre, double *y)
+{
+    int64_t P = T * topk;
+    for (int64_t i = 0; i < P * H; ++i)
+        pre[i] = 0.0;
+    for (int64_t e = 0; e < E; ++e) {
+        const uint8_t *we = w2_fp4 + e * H * (I / 2);
+        const uint8_t *se = w2_scale + e * H * (I / 32);
+        for (int64_t h = 0; h < H; ++h) {
+            mxfp4_dequant_row(we, se, I, h, w_row);
+            for (int64_t p = 0; p < P; ++p)
+                if (ids[p] == e)
+                    pre[p * H + h] = dot_row(a, DT_BF16, p, I, w_row);
+        }
+    }
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int64_t s = 0; s < topk; ++s) {
+                int32_t e = ids[t * topk + s];
+                if (e >= 0 && e < E)
+                    acc += (double)w[t * topk + s] * pre[(t * topk + s) * H + h];
+            }
+            y[t * H + h] = acc;
+        }
+}
+
+/* The same definition evaluated at (ts[i], hs[i]). */
+void oracle_mxfp4_moe_stage2_sampled(const uint16_t *a, const int32_t *ids, const float *w,
+                                     const uint8_t *w2_fp4, const uint8_t *w2_scale, int64_t topk,
+                                     int64_t E, int64_t H, int64_t I, const int64_t *ts,
+                                     const int64_t *hs, int64_t count, float *w_row, double *out)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        double acc = 0.0;
+        for (int64_t s = 0; s < topk; ++s) {
+            int64_t p = ts[i] * topk + s;
+            int32_t e = ids[p];
+            if (e < 0 || e >= E)
+                continue;
+            mxfp4_dequant_row(w2_fp4 + (int64_t)e * H * (I / 2), w2_scale + (int64_t)e * H * (I / 32),
+                              I, hs[i], w_row);
+            acc += (double)w[p] * dot_row(a, DT_BF16, p, I, w_row);
+        }
+        out[i] = acc;
+    }
 }

@@ -165,6 +165,24 @@ def moe_inputs(T, E, topk, N, K, seed=0, exp_lo=118, exp_hi=126):
                 w_scale=w_scale, T=T, E=E, topk=topk, N=N, K=K)
 
 
+def moe_stage2_inputs(T, E, topk, H, I, seed=0, exp_lo=118, exp_hi=126):
+    """MoE stage-2 operands: the stage-1 activation rows a [T][topk][I] ~ N(0,1)
+    in bfloat16, ids as in moe_inputs, routing weights [T][topk] fp32 (uniform
+    keys normalised to sum 1 per token), W2 codes [E][H][I/2] uniform bytes,
+    E8M0 scales [E][H][I/32] uniform in [exp_lo, exp_hi].  Draw order: a, ids,
+    weights, codes, scales."""
+    assert I % 32 == 0 and topk <= E
+    rng = np.random.default_rng(seed)
+    a = to_act_bits(rng.standard_normal((T, topk, I), dtype=np.float32), BF16)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :topk].astype(np.int32)
+    r = rng.random((T, topk)).astype(np.float32) + np.float32(0.05)
+    w = (r / r.sum(axis=1, keepdims=True)).astype(np.float32)
+    w2_fp4 = rng.integers(0, 256, size=(E, H, I // 2), dtype=np.uint8)
+    w2_scale = rng.integers(exp_lo, exp_hi + 1, size=(E, H, I // 32), dtype=np.uint8)
+    return dict(a=np.ascontiguousarray(a), ids=np.ascontiguousarray(ids), w=np.ascontiguousarray(w),
+                w2_fp4=w2_fp4, w2_scale=w2_scale, T=T, E=E, topk=topk, H=H, I=I)
+
+
 def routed_group_rows(T, E, topk, seed=0):
     """Rows per expert of a uniform top-k routing (the recipe of moe_inputs)."""
     rng = np.random.default_rng(seed)
