@@ -417,6 +417,41 @@ def bench_moe(wkey: str, steps: int, warmup: int, reps: int, act: int = 0):
     return res, d
 
 
+def bench_moe2(wkey: str, steps: int, warmup: int, reps: int):
+    import weight_only_bit_amd as wob
+    torch = _torch()
+    w = wl.BY_KEY[wkey]
+    d = w.make(seed=0)
+    T, E, topk, H, I = d["T"], d["E"], d["topk"], d["H"], d["I"]
+    nbytes = wl.moe_stage2_bytes(T, E, topk, H, I)
+    copies = copies_for(nbytes)
+    flops = 2 * T * topk * H * I
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    bufs = [dict(a=dev(d["a"].view(np.int16)).view(torch.bfloat16), ids=dev(d["ids"]),
+                 w=dev(d["w"]), w2=dev(d["w2_fp4"]), s2=dev(d["w2_scale"]))
+            for _ in range(copies)]
+    ys = [torch.empty((T, H), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+    ws = torch.empty(max(wob.moe_stage2_workspace_size(T, topk, E, H, I), 16), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(c):
+        b = bufs[c]
+        wob.mxfp4_moe_stage2(b["a"], b["ids"], b["w"], b["w2"], b["s2"], out=ys[c], workspace=ws)
+
+    t = time_steps(step, steps, warmup, copies, reps)
+    res = dict(workload=w.desc, T=T, E=E, topk=topk, H=H, I=I, dtype="bf16 x mxfp4",
+               bytes_per_call=nbytes, flops_per_call=flops, **t.summary(),
+               tflops=round(flops / (t.ms * 1e-3) / 1e12, 2))
+    # a step is routing + GEMM + combine: conservative for the GEMM alone
+    res["roofline"] = _roofline_mfma(flops, t, committed_traffic(wkey, "moe"))
+    del bufs, ys
+    torch.cuda.empty_cache()
+    return res, d
+
+
 # --- CPU baseline: the oracle as it stands, one host thread ----------------------
 
 def _cpu_model() -> str:
@@ -527,7 +562,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    run = {"w4a16": bench_w4a16, "grouped": bench_grouped, "moe": bench_moe}
+    run = {"w4a16": bench_w4a16, "grouped": bench_grouped, "moe": bench_moe, "moe2": bench_moe2}
     head = wl.BY_KEY[args.workload]
     res, d = run[head.kind](head.key, args.steps, args.warmup, args.reps)
     skinny = head.kind == "w4a16" and d["M"] <= 8

@@ -183,6 +183,42 @@ int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
                    int64_t K, int act, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace mxfp4_moe_stage2 needs: the routing scratch of
+ * stage 1 plus T*topk*H fp32 per-pair results.  0 for arguments it refuses
+ * on sight (T < 0, topk outside 1..64, E outside 1..4096, H or I negative).
+ */
+size_t mxfp4_moe_stage2_workspace_size(int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I);
+
+/*
+ * MoE stage 2, BF16 x MXFP4: the down projection of the stage-1 activation
+ * rows with the routing-weight combine,
+ *   y[t][h] = sum over s < topk with e = topk_ids[t][s] in [0, E) of
+ *             topk_weights[t][s] * sum_i a[t][s][i] * w2_e(h, i),
+ *   w2_e(h, i) = e2m1(code) * 2^(w2_scale[e][h][i/32] - 127) as in stage 1.
+ * The MXFP4 page above names its kernel stage 1 (summary, Test); the second
+ * stage is this library's reading of the MoE layer it belongs to: each
+ * routed row of the stage-1 output (act == WOB_ACT_SILU_MUL, I = N/2) is
+ * multiplied with its expert's W2, weighted, and the token's slots summed.
+ *
+ *  a [T][topk][I] bf16; topk_ids [T][topk] int32 (device, as for stage 1);
+ *  topk_weights [T][topk] fp32 (device); w2_fp4 [E][H][I/2] uint8 (even i in
+ *  the low nibble); w2_scale [E][H][I/32] uint8 E8M0; y [T][H] bf16.
+ *  Slots whose id lies outside [0, E) contribute nothing.  Each slot's
+ *  products accumulate in fp32; the weighted slots are summed in slot order
+ *  in fp32 and rounded once to bf16 (deterministic).
+ *  I % 64 == 0, I >= 64, H % 16 == 0, T >= 0, 1 <= topk <= 64,
+ *  1 <= E <= 4096, T*topk*I*2 and H*I/2 below 2^32 (else WOB_INVALID_ARG).
+ *  T == 0 or H == 0 is a no-op returning WOB_OK.
+ *  workspace: device memory of at least mxfp4_moe_stage2_workspace_size(T,
+ *  topk, E, H, I) bytes, 16-byte aligned; contents on entry do not matter.
+ *  Calls sharing one workspace must be ordered on one stream.
+ */
+int mxfp4_moe_stage2(const void *a, const int32_t *topk_ids, const float *topk_weights,
+                     const uint8_t *w2_fp4, const uint8_t *w2_scale, void *y, int64_t T,
+                     int64_t topk, int64_t E, int64_t H, int64_t I, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
  * mxfp4_moe_gemm without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): the routing scratch lives in a static

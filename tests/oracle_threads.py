@@ -75,3 +75,19 @@ def mxfp4_moe_gemm_sampled(oracle, d, ts, ss, ns, ids=None, threads=None):
     with cf.ThreadPoolExecutor(threads or host_threads()) as ex:
         list(ex.map(run, _slices(ts.size, 4 * (threads or host_threads()), 1)))
     return out
+
+
+def mxfp4_moe_stage2_sampled(oracle, d, ts, hs, threads=None):
+    """The oracle's fp64 MoE stage-2 output at (ts[i], hs[i])."""
+    ts, hs = (np.asarray(v, np.int64) for v in (ts, hs))
+    out = np.empty(ts.shape, np.float64)
+
+    def run(lo_hi):
+        lo, hi = lo_hi
+        out[lo:hi] = oracle.mxfp4_moe_stage2_sampled(d["a"], d["ids"], d["w"], d["w2_fp4"],
+                                                     d["w2_scale"], d["topk"], d["E"], d["H"],
+                                                     d["I"], ts[lo:hi], hs[lo:hi])
+
+    with cf.ThreadPoolExecutor(threads or host_threads()) as ex:
+        list(ex.map(run, _slices(ts.size, 4 * (threads or host_threads()), 1)))
+    return out

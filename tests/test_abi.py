@@ -231,3 +231,23 @@ def test_binding_grouped_and_moe_shape_checks(wobpkg):
         wobpkg.mxfp4_moe_gemm(xb, ids, w, ws)
     with pytest.raises(ValueError, match="w_scale"):
         wobpkg.mxfp4_dequant(w[0], ws[0, :, :2])
+
+
+def test_moe_stage2_checks(L):
+    """MoE stage 2 refuses bad shapes, pointers and workspaces before any
+    device access."""
+    f = _Fake()
+    p = f.p
+    need = L.lib().mxfp4_moe_stage2_workspace_size(1024, 4, 32, 2880, 2880)
+    assert need >= 1024 * 4 * 2880 * 4  # the fp32 per-pair rows
+    assert L.lib().mxfp4_moe_stage2_workspace_size(4, 0, 32, 64, 64) == 0
+    call = lambda I=64, H=32, ws=need, T=4, wp=p: L.lib().mxfp4_moe_stage2(
+        p, p, wp, p, p, p, T, 4, 32, H, I, p, ws, None)
+    assert call(I=96) == L.INVALID_ARG    # the K tile is 64 wide
+    assert call(I=32) == L.INVALID_ARG
+    assert call(H=24) == L.INVALID_ARG
+    assert call(T=1 << 20, I=1 << 10) == L.INVALID_ARG  # gathered rows past 32-bit offsets
+    assert call(ws=16) == L.INVALID_ARG
+    assert call(wp=None) == L.INVALID_ARG
+    assert call(T=0) == L.OK
+    assert call(H=0) == L.OK

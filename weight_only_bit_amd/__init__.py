@@ -8,6 +8,7 @@ fallback.
     y = gemm(x, qweight, scales, qzeros, group_size)        # W4A16
     y = gemm_grouped(x, m_offsets, qweight, scales, qzeros, group_size)
     y = mxfp4_moe_gemm(x, topk_ids, w_fp4, w_scale)         # MoE stage 1
+    y = mxfp4_moe_stage2(a, topk_ids, topk_weights, w2_fp4, w2_scale)  # MoE stage 2
 
 Layouts are those of ``include/weight_only_bit.h``.
 """
@@ -21,7 +22,8 @@ from ._lib import (ACT_NONE, ACT_SILU_MUL, BF16, DTYPE, F16, F32, INVALID_ARG, O
                    WobError)
 
 __all__ = [
-    "gemm", "gemm_grouped", "mxfp4_moe_gemm", "moe_workspace_size", "w4a16_dequant",
+    "gemm", "gemm_grouped", "mxfp4_moe_gemm", "moe_workspace_size", "mxfp4_moe_stage2",
+    "moe_stage2_workspace_size", "w4a16_dequant",
     "mxfp4_dequant", "stream_read", "device_check", "WobError", "WobDtypeError", "WobArgError",
     "PATH_AUTO", "PATH_SKINNY", "PATH_TILED", "ACT_NONE", "ACT_SILU_MUL",
 ]
@@ -200,6 +202,46 @@ def mxfp4_moe_gemm(x, topk_ids, w_fp4, w_scale, out=None, workspace=None, act: i
             _ptr(x), _ptr(topk_ids), _ptr(w_fp4), _ptr(w_scale), _ptr(out), T, topk, E, N, K, act,
             _ptr(workspace), ws_bytes, _stream(dev))
     _lib.check(st, "mxfp4_moe_gemm")
+    return out
+
+
+def moe_stage2_workspace_size(T: int, topk: int, E: int, H: int, I: int) -> int:
+    """Bytes of workspace mxfp4_moe_stage2 needs (0 for arguments it refuses)."""
+    return int(_lib.lib().mxfp4_moe_stage2_workspace_size(T, topk, E, H, I))
+
+
+def mxfp4_moe_stage2(a, topk_ids, topk_weights, w2_fp4, w2_scale, out=None, workspace=None):
+    """MoE stage 2: a [T,topk,I] bf16 (the stage-1 activation rows), topk_ids
+    [T,topk] int32, topk_weights [T,topk] float32, w2_fp4 [E,H,I/2] uint8,
+    w2_scale [E,H,I/32] uint8 (E8M0) -> y [T,H] bf16 = sum over slots of
+    weight * (a row . expert's W2)."""
+    torch = _torch()
+    if a.dim() != 3 or topk_ids.dim() != 2 or w2_fp4.dim() != 3:
+        raise ValueError("a must be [T, topk, I], topk_ids [T, topk] and w2_fp4 [E, H, I/2]")
+    _want(a, "a", tuple(a.shape), (torch.bfloat16,))
+    T, topk, I = a.shape
+    E, H = w2_fp4.shape[0], w2_fp4.shape[1]
+    if I % 32 != 0:
+        raise ValueError(f"I={I} must be a multiple of 32 (one E8M0 scale per 32)")
+    _want(topk_ids, "topk_ids", (T, topk), (torch.int32,))
+    _want(topk_weights, "topk_weights", (T, topk), (torch.float32,))
+    _want(w2_fp4, "w2_fp4", (E, H, I // 2), (torch.uint8,))
+    _want(w2_scale, "w2_scale", (E, H, I // 32), (torch.uint8,))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=a.device)
+    _want(out, "out", (T, H), (torch.bfloat16,))
+    need = moe_stage2_workspace_size(T, topk, E, H, I)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if ws_bytes < need:
+        raise ValueError(f"workspace holds {ws_bytes} bytes; {need} are needed")
+    dev = _check_device(a, topk_ids, topk_weights, w2_fp4, w2_scale, out, workspace)
+    with torch.cuda.device(dev):
+        st = _lib.lib().mxfp4_moe_stage2(
+            _ptr(a), _ptr(topk_ids), _ptr(topk_weights), _ptr(w2_fp4), _ptr(w2_scale), _ptr(out),
+            T, topk, E, H, I, _ptr(workspace), ws_bytes, _stream(dev))
+    _lib.check(st, "mxfp4_moe_stage2")
     return out
 
 

@@ -21,6 +21,7 @@ EXPORTS = [
     "wob_status_str", "wob_last_error", "wob_device_check",
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_grouped",
     "mxfp4_moe_gemm_workspace_size", "mxfp4_moe_gemm", "mxfp4_moe_gemm_noalloc",
+    "mxfp4_moe_stage2_workspace_size", "mxfp4_moe_stage2",
     "w4a16_dequant", "mxfp4_dequant", "wob_stream_read",
 ]
 
@@ -42,6 +43,9 @@ _SIGNATURES = {
                             _vp]),
     "mxfp4_moe_gemm_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i,
                                     _vp]),
+    "mxfp4_moe_stage2_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "mxfp4_moe_stage2": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _sz,
+                              _vp]),
     "w4a16_dequant": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _i64, _i64, _i64, _vp]),
     "mxfp4_dequant": (_i, [_vp, _vp, _vp, _i64, _i64, _vp]),
     "wob_stream_read": (_i, [_vp, _sz, _vp, _vp]),

@@ -316,6 +316,51 @@ int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
                     "mxfp4 moe");
 }
 
+size_t mxfp4_moe_stage2_workspace_size(int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I)
+{
+    if (T < 0 || topk < 1 || E < 1 || H < 0 || I < 0 || T > INT_MAX / 64 || topk > 64 ||
+        E > 4096 || H > INT_MAX / 2)
+        return 0;
+    return wob::moe_stage2_workspace_bytes(T, topk, E, H);
+}
+
+int mxfp4_moe_stage2(const void *a, const int32_t *topk_ids, const float *topk_weights,
+                     const uint8_t *w2_fp4, const uint8_t *w2_scale, void *y, int64_t T,
+                     int64_t topk, int64_t E, int64_t H, int64_t I, void *workspace,
+                     size_t workspace_bytes, void *stream)
+{
+    if (T < 0 || topk < 1 || E < 1 || H < 0 || I < 64)
+        return fail(WOB_INVALID_ARG, "bad shape T=%lld topk=%lld E=%lld H=%lld I=%lld",
+                    (long long)T, (long long)topk, (long long)E, (long long)H, (long long)I);
+    if (I % 64 != 0 || H % 16 != 0)
+        return fail(WOB_INVALID_ARG, "need I %% 64 == 0 and H %% 16 == 0 (I=%lld H=%lld)",
+                    (long long)I, (long long)H);
+    // 32-bit in-kernel offsets: gathered rows of a (T*topk*I*2 bytes) and one
+    // expert's codes (H*I/2 bytes).
+    if (T > INT_MAX / 64 || topk > 64 || E > 4096 || H > INT_MAX / 2 || I > INT_MAX / 2 ||
+        T * topk * I * 2 > (int64_t)UINT32_MAX || H * (I / 2) > (int64_t)UINT32_MAX ||
+        E * H * (I / 2) > ((int64_t)1 << 40))
+        return fail(WOB_INVALID_ARG, "shape too large");
+    if (T == 0 || H == 0)
+        return ok();
+    if (!a || !topk_ids || !topk_weights || !w2_fp4 || !w2_scale || !y)
+        return fail(WOB_INVALID_ARG, "null operand pointer");
+    if (!aligned16(a) || !aligned16(topk_ids) || !aligned16(topk_weights) || !aligned16(w2_fp4) ||
+        !aligned16(w2_scale) || !aligned16(y))
+        return fail(WOB_INVALID_ARG, "operand pointers must be 16-byte aligned");
+    const size_t need = wob::moe_stage2_workspace_bytes(T, topk, E, H);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+        return fail(WOB_INVALID_ARG, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    int s = arch_gate();
+    if (s != WOB_OK)
+        return s;
+    return launched(wob::launch_mxfp4_moe_stage2(a, topk_ids, topk_weights, w2_fp4, w2_scale, y,
+                                                 (int)T, (int)topk, (int)E, (int)H, (int)I,
+                                                 workspace, static_cast<hipStream_t>(stream)),
+                    "mxfp4 moe stage 2");
+}
+
 int mxfp4_moe_gemm_noalloc(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
                            const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E,
                            int64_t N, int64_t K, int act, void *stream)

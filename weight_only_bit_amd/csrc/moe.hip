@@ -244,6 +244,144 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
                                          n0, smem, tl);
 }
 
+// ---- Stage 2: down projection with the routing-weight combine ------------
+//
+// Reading (the pages define stage 1 only): for token t and slot s with
+// expert e = ids[t][s] in [0, E),
+//     pre[t*topk + s][h] = sum_i a[t][s][i] * w2_e[h][i]
+//     y[t][h] = sum over valid s of w[t][s] * pre[t*topk + s][h]
+// The GEMM is the stage-1 tile kernel with activation rows gathered by routed
+// pair (row p of a [T*topk][I]) instead of by token, and an fp32 epilogue
+// into `pre` (workspace).  A second kernel sums each token's slots in slot
+// order, so the result does not depend on timing.
+
+// A tile's rows of pre straight from the accumulators: the lane holds
+// D[n = 32 NB w + 32 nb + 8 g4 + 4 h + j][m = 32 mb + nl] in register 4 g4 + j
+// of block (nb, mb), i.e. four consecutive outputs of one row: one 16-byte
+// store each.  Rows past the tile's count and columns past H are not written.
+template <int NB, int MB>
+__device__ __forceinline__ void tile_store_rows_f32(const float16_t (&acc)[NB][MB], float *pre,
+                                                    const int32_t *pairs, int rows, int n0, int H,
+                                                    const TileLane &tl)
+{
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int r = 32 * mb + tl.nl;
+        if (r >= rows)
+            continue;
+        float *row = pre + (size_t)pairs[r] * H;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int n = n0 + 32 * NB * tl.wave + 32 * nb + 8 * g4 + 4 * tl.h;
+                if (n < H) {
+                    const float16_t &v = acc[nb][mb];
+                    *reinterpret_cast<float4_t *>(row + n) =
+                        float4_t{v[4 * g4 + 0], v[4 * g4 + 1], v[4 * g4 + 2], v[4 * g4 + 3]};
+                }
+            }
+    }
+}
+
+constexpr int MOE2_NB = 3; // 384-row weight tiles (2880 = 7.5 of them)
+
+template <int MB>
+__device__ __forceinline__ void moe2_run(const FmtFP4<false, MOE2_NB> &fmt, const int32_t *pairs,
+                                         int rows, const uint16_t *a, float *pre, int I, int H,
+                                         int n0, uint8_t *smem, const TileLane &tl)
+{
+    GatherRows<MB> g;
+    g.pairs = pairs;
+    g.base = nullptr;
+    g.ld = 0;
+#pragma unroll
+    for (int i = 0; i < 2 * MB; ++i)
+        g.xo[i] = (uint32_t)pairs[min(16 * i + tl.rl, rows - 1)] * (uint32_t)I * 2u;
+    float16_t acc[MOE2_NB][MB];
+    tile_mainloop<DT_BF16, MOE2_NB, MB>(fmt, g, reinterpret_cast<const uint8_t *>(a), I, n0, H,
+                                        smem, tl, acc);
+    tile_store_rows_f32<MOE2_NB, MB>(acc, pre, pairs, rows, n0, H, tl);
+}
+
+template <int MB>
+__device__ __forceinline__ void moe2_dispatch(int mb, const FmtFP4<false, MOE2_NB> &fmt,
+                                              const int32_t *pairs, int rows, const uint16_t *a,
+                                              float *pre, int I, int H, int n0, uint8_t *smem,
+                                              const TileLane &tl)
+{
+    if constexpr (MB > 1) {
+        if (mb < MB) {
+            moe2_dispatch<MB - 1>(mb, fmt, pairs, rows, a, pre, I, H, n0, smem, tl);
+            return;
+        }
+    }
+    moe2_run<MB>(fmt, pairs, rows, a, pre, I, H, n0, smem, tl);
+}
+
+// One (expert tile, weight-row tile) pair per workgroup, as in stage 1.
+__global__ __launch_bounds__(TL_THREADS, 1) void moe_stage2_kernel(
+    const uint16_t *__restrict__ a, const uint8_t *__restrict__ w_fp4,
+    const uint8_t *__restrict__ w_scale, float *__restrict__ pre, const int32_t *__restrict__ hdr,
+    const int4 *__restrict__ tiles, const int32_t *__restrict__ sorted, int E, int H, int I,
+    int n_nt, int nxcd)
+{
+    constexpr int TW = TileGeo<MOE2_NB>::TN;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int t = xcd_tile(hdr[0] * n_nt, nxcd);
+    if (t < 0)
+        return;
+    const int i = t / n_nt;
+    const int n0 = (t - i * n_nt) * TW;
+    const int4 te = tiles[i];
+    const int e = te.x, rows = te.z;
+    if (e >= E)
+        return; // ids outside [0, E): the combine skips these slots
+    const TileLane tl;
+    const FmtFP4<false, MOE2_NB> fmt(w_fp4 + (size_t)e * H * (I >> 1),
+                                     w_scale + (size_t)e * H * (I >> 5), H, I, n0, tl);
+    moe2_dispatch<moe_mb_max<false>()>((rows + 31) >> 5, fmt, sorted + te.y, rows, a, pre, I, H,
+                                       n0, smem, tl);
+}
+
+// y[t][h .. h+7] = sum over valid slots s (in order) of w[t][s] * pre[t*topk + s][h ..],
+// rounded once to bfloat16.  One thread per 8 outputs (H % 16 == 0).
+constexpr int CB_THREADS = 256;
+
+__global__ __launch_bounds__(CB_THREADS) void moe_combine_kernel(
+    const float *__restrict__ pre, const int32_t *__restrict__ ids, const float *__restrict__ w,
+    uint16_t *__restrict__ y, int T, int topk, int E, int H)
+{
+    const int H8 = H >> 3;
+    const int64_t idx = (int64_t)blockIdx.x * CB_THREADS + threadIdx.x;
+    if (idx >= (int64_t)T * H8)
+        return;
+    const int t = (int)(idx / H8);
+    const int c = (int)(idx - (int64_t)t * H8) * 8;
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        acc[j] = 0.f;
+    for (int s = 0; s < topk; ++s) {
+        const int p = t * topk + s;
+        if ((unsigned)ids[p] >= (unsigned)E)
+            continue;
+        const float ws = w[p];
+        const float4_t *src = reinterpret_cast<const float4_t *>(pre + (size_t)p * H + c);
+        const float4_t v0 = src[0], v1 = src[1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[j] = fmaf(ws, v0[j], acc[j]);
+            acc[4 + j] = fmaf(ws, v1[j], acc[4 + j]);
+        }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        o[j] = f32x2_to_act2<DT_BF16>(acc[2 * j], acc[2 * j + 1]);
+    *reinterpret_cast<u32x4 *>(y + (size_t)t * H + c) = o;
+}
+
 // ---- Decode path: at most MG_TOKENS tokens --------------------------------
 //
 // With a handful of tokens every expert holds one or two routed rows, so the
@@ -580,6 +718,55 @@ hipError_t moe_scratch(void **ptr)
     }
     *ptr = p;
     return hipSuccess;
+}
+
+size_t moe_stage2_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t H)
+{
+    const size_t route = (moe_workspace_bytes(T, topk, E) + 255) & ~(size_t)255;
+    return route + (size_t)(T * topk) * (size_t)H * sizeof(float);
+}
+
+hipError_t launch_mxfp4_moe_stage2(const void *a, const int32_t *ids, const float *w,
+                                   const uint8_t *w_fp4, const uint8_t *w_scale, void *y, int T,
+                                   int topk, int E, int H, int I, void *workspace,
+                                   hipStream_t stream)
+{
+    const int64_t P = (int64_t)T * topk;
+    const MoeWs ws = carve(workspace, P, E);
+    float *pre = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
+                                           ((moe_workspace_bytes(T, topk, E) + 255) & ~(size_t)255));
+    const size_t route_lds = (size_t)(3 * (E + 1)) * sizeof(int);
+    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(ROUTE_THREADS), route_lds, stream, ids,
+                       (int)P, E, moe_tm<false>(), ws.hdr, ws.tiles, ws.sorted);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    constexpr int LDS = TileGeo<MOE2_NB>::lds_bytes(TileGeo<MOE2_NB>::MB_MAX);
+    static_assert(LDS <= 160 * 1024, "tile fits the LDS");
+    static std::atomic<uint64_t> lds_set{0};
+    if (const hipError_t e = lds_optin(reinterpret_cast<const void *>(moe_stage2_kernel), LDS,
+                                       lds_set);
+        e != hipSuccess)
+        return e;
+    const int tw = TileGeo<MOE2_NB>::TN;
+    const int n_nt = (H + tw - 1) / tw;
+    const int nxcd = device_topology().xcds;
+    const int64_t grid = (int64_t)nxcd * (((int64_t)max_tiles(P, E) * n_nt + nxcd - 1) / nxcd);
+    if (grid > INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(moe_stage2_kernel, dim3((unsigned)grid), dim3(TL_THREADS), (size_t)LDS,
+                       stream, static_cast<const uint16_t *>(a), w_fp4, w_scale, pre, ws.hdr,
+                       ws.tiles, ws.sorted, E, H, I, n_nt, nxcd);
+    err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    const int64_t outs = (int64_t)T * (H / 8);
+    const int64_t cgrid = (outs + CB_THREADS - 1) / CB_THREADS;
+    if (cgrid > INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)cgrid), dim3(CB_THREADS), 0, stream, pre,
+                       ids, w, static_cast<uint16_t *>(y), T, topk, E, H);
+    return hipGetLastError();
 }
 
 size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t E)

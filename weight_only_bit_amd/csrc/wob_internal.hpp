@@ -59,6 +59,12 @@ hipError_t launch_w4a16_grouped(const W4Args &a, const int64_t *m_offsets, int n
 
 // MoE stage 1, BF16 x MXFP4.
 size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t E);
+// MoE stage 2: routing scratch plus the fp32 per-pair rows `pre` [T*topk][H].
+size_t moe_stage2_workspace_bytes(int64_t T, int64_t topk, int64_t E, int64_t H);
+hipError_t launch_mxfp4_moe_stage2(const void *a, const int32_t *ids, const float *w,
+                                   const uint8_t *w_fp4, const uint8_t *w_scale, void *y, int T,
+                                   int topk, int E, int H, int I, void *workspace,
+                                   hipStream_t stream);
 // The static routing scratch of the allocation-free entry point: its size,
 // and its address on the current device (looked up on first use per device).
 size_t moe_scratch_bytes();

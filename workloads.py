@@ -208,7 +208,7 @@ def grouped_bytes(total_m, E, N, K, g, act_bytes=2):
 @dataclass(frozen=True)
 class Workload:
     key: str
-    kind: str  # "w4a16" or "moe"
+    kind: str  # "w4a16", "grouped", "moe" or "moe2"
     desc: str
     params: dict
 
@@ -216,6 +216,8 @@ class Workload:
         p = dict(self.params)
         if self.kind == "w4a16":
             return w4a16_inputs(p["M"], p["N"], p["K"], p["g"], p["dtype"], seed=seed)
+        if self.kind == "moe2":
+            return moe_stage2_inputs(p["T"], p["E"], p["topk"], p["H"], p["I"], seed=seed)
         if self.kind == "grouped":
             rows = routed_group_rows(p["T"], p["E"], p["topk"], seed=seed)
             return w4a16_grouped_inputs(rows, p["N"], p["K"], p["g"], p["dtype"], seed=seed)
@@ -253,6 +255,13 @@ EXTRA_WORKLOADS = [
     Workload("moe_decode", "moe",
              "MoE stage-1 BF16xMXFP4 decode: 4 tokens, 32 experts, top-4, K=2880, N=5760",
              dict(T=4, E=32, topk=4, N=5760, K=2880)),
+    # MoE stage 2 after the stage-1 shape: the down projection of the
+    # 2880-wide activation rows back to the 2880-wide model dimension, with
+    # the routing-weight combine (a reading: the pages define stage 1 only).
+    Workload("moe_stage2", "moe2",
+             "MoE stage-2 BF16xMXFP4 1024 tokens, 32 experts, top-4, I=2880, H=2880, "
+             "routing-weight combine",
+             dict(T=1024, E=32, topk=4, H=2880, I=2880)),
     # The grouped GEMM on an MoE-like uint4 configuration: the MoE stage-1
     # shape with W4A16 experts, rows per expert from a uniform top-4 routing.
     Workload("grouped_moe_like", "grouped",
@@ -270,6 +279,12 @@ def w4a16_bytes(M, N, K, g, act_bytes=2, symmetric=False):
     G = K // g
     b = N * K // 2 + act_bytes * N * G + (0 if symmetric else N * G // 2)
     return b + act_bytes * M * K + act_bytes * M * N
+
+
+def moe_stage2_bytes(T, E, topk, H, I):
+    """Algorithmic bytes of one MoE stage-2 call: W2 codes and E8M0 scales, the
+    activation rows, ids, routing weights and y."""
+    return E * H * I // 2 + E * H * I // 32 + 2 * T * topk * I + 8 * T * topk + 2 * T * H
 
 
 def moe_bytes(T, E, topk, N, K):
