@@ -68,6 +68,7 @@ MALL_BYTES = 256 << 20         # Infinity Cache
 REUSE_BYTES = 2 * MALL_BYTES   # bytes touched between two uses of one operand copy
 MAX_COPIES = 512               # tiny calls: the cache cannot be defeated; labelled hot
 SETTLE_S = 0.3                 # untimed replays before each timed series (clock ramp)
+_settle_s = SETTLE_S           # --settle-s
 FETCH_FACTOR_DEFAULT = 2.0     # FETCH_SIZE reads half of a device copy's bytes on this part
 TRAFFIC_SOURCE = ("committed rocprofv3 counters (profiles/traffic.json: FETCH_SIZE x fetch "
                   "factor + WRITE_SIZE per dispatch); null when the kernel sources changed "
@@ -190,7 +191,7 @@ def time_steps(step, steps: int, warmup: int, copies: int, reps: int) -> Timing:
     # untimed: whole cycles until the clocks have settled (the first replays
     # after an idle period run up to a quarter slower while they ramp)
     t_settle = time.perf_counter()
-    while time.perf_counter() - t_settle < SETTLE_S:
+    while time.perf_counter() - t_settle < _settle_s:
         for g in graphs:
             g.replay()
         torch.cuda.synchronize()
@@ -533,6 +534,8 @@ def main():
     ap.add_argument("--workload", default="decode_gemv", choices=[w.key for w in wl.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="seconds of untimed whole-cycle replays before each timed series")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before timing, run three device-to-device copies of this many MiB "
                          "(untimed): the known-size reference for the profiler's byte counters")
@@ -547,6 +550,8 @@ def main():
         print("bench.py: --steps and --reps must be >= 1, --warmup >= 0", file=sys.stderr)
         sys.exit(2)
 
+    global _settle_s
+    _settle_s = max(0.0, args.settle_s)
     torch = _torch()
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -565,6 +570,7 @@ def main():
     run = {"w4a16": bench_w4a16, "grouped": bench_grouped, "moe": bench_moe, "moe2": bench_moe2}
     head = wl.BY_KEY[args.workload]
     res, d = run[head.kind](head.key, args.steps, args.warmup, args.reps)
+    print(f"bench.py: {head.key} {res['us_per_call']} us", file=sys.stderr, flush=True)
     skinny = head.kind == "w4a16" and d["M"] <= 8
     line = dict(
         metric=METRIC,
@@ -597,6 +603,7 @@ def main():
                 if not args.no_cpu_baseline and w in wl.WORKLOADS:
                     r["cpu_baseline"] = cpu_baseline(w.key, dd)
                 others[w.key] = r
+                print(f"bench.py: {w.key} {r['us_per_call']} us", file=sys.stderr, flush=True)
             except Exception as e:  # report, do not hide: the entry says what failed
                 others[w.key] = dict(workload=w.desc, error=f"{type(e).__name__}: {e}")
         try:
