@@ -183,6 +183,21 @@ int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
                    int64_t K, int act, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mxfp4_moe_gemm with a chosen tile height tile_m: each expert's routed rows
+ * are padded to a multiple of tile_m (the MFMA block height of the expert
+ * tiles), 16 or 32 (else WOB_INVALID_ARG).  Source: MXFP4 page above, Test
+ * Plan / Test Result (the stage-1 kernel is built and tested per tile height).
+ * mxfp4_moe_gemm is tile_m = 32.  Same function, arguments, workspace and
+ * errors; decode batches (T <= 8) take the memory-bound kernel whatever
+ * tile_m is.  16 wastes fewer products on padding but measures slower on
+ * MI355X at every batch size tried (16 to 1024 tokens).
+ */
+int mxfp4_moe_gemm_tile_m(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
+                          const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E,
+                          int64_t N, int64_t K, int act, int tile_m, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace mxfp4_moe_stage2 needs: the routing scratch of
  * stage 1 plus T*topk*H fp32 per-pair results.  0 for arguments it refuses
  * on sight (T < 0, topk outside 1..64, E outside 1..4096, H or I negative).

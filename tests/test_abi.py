@@ -126,6 +126,12 @@ def test_moe_checks(L):
     assert act(1, N=48) == L.INVALID_ARG    # silu(gate) * up needs N % 32 == 0
     assert call(ws=0) == L.INVALID_ARG
     assert call(T=0) == L.OK
+    tm = lambda t, T=4, K=64: L.lib().mxfp4_moe_gemm_tile_m(p, p, p, p, p, T, 4, 32, 32, K, 0, t,
+                                                             p, need, None)
+    for bad_tm in (0, 8, 24, 64, -16):
+        assert tm(bad_tm) == L.INVALID_ARG, bad_tm
+    assert tm(16, K=48) == L.INVALID_ARG    # the other checks still apply
+    assert tm(16, T=0) == L.OK and tm(32, T=0) == L.OK
 
 
 def test_grouped_checks(L):
@@ -227,6 +233,8 @@ def test_binding_grouped_and_moe_shape_checks(wobpkg):
         wobpkg.mxfp4_moe_gemm(xb, ids, w, ws, workspace=torch.zeros(4, dtype=torch.uint8))
     with pytest.raises(ValueError, match="activation"):
         wobpkg.mxfp4_moe_gemm(xb, ids, w, ws, act=5)
+    with pytest.raises(ValueError, match="tile_m"):
+        wobpkg.mxfp4_moe_gemm(xb, ids, w, ws, tile_m=64)
     with pytest.raises(ValueError, match="device"):
         wobpkg.mxfp4_moe_gemm(xb, ids, w, ws)
     with pytest.raises(ValueError, match="w_scale"):

@@ -3,10 +3,12 @@ the C ABI.
 
 Bar: |y - y_ref| <= 1e-3 + 1e-2 * max|y_ref| per element, no NaN/Inf, and every
 (token, slot) row written exactly where it belongs.  The matrix follows the
-MXFP4 MoE page (section Test: tile heights 16, 32 and 64 rows per expert; the
-store-guard fix for a tile that overhangs the weight rows) widened to skewed
-and empty experts, top-1 routing, out-of-range ids, ragged N and K, and the
-full 1024-token, 32-expert, top-4, K=2880, N=5760 shape on sampled outputs.
+MXFP4 MoE page (section Test: the kernel per tile height x activation;
+experts holding 16, 32 and 64 rows; the store-guard fix for a tile that
+overhangs the weight rows) widened to skewed and empty experts, top-1
+routing, out-of-range ids, ragged N and K, and the full 1024-token,
+32-expert, top-4, K=2880, N=5760 shape on sampled outputs.  The tile-kernel
+tests run at both tile heights the library builds (tile_m 16 and 32).
 """
 import numpy as np
 import pytest
@@ -26,7 +28,10 @@ def wob():
     return w
 
 
-def _run(wob, d, ids=None):
+TILE_M = [32, 16]
+
+
+def _run(wob, d, ids=None, tile_m=32):
     """Run with NaN-filled guard rows around y; return y's bf16 bits [T, topk, N]."""
     torch = torch_mod()
     T, topk, N = d["T"], d["topk"], d["N"]
@@ -35,7 +40,7 @@ def _run(wob, d, ids=None):
     out.fill_(float("nan"))
     y = out[1:T * topk + 1].view(T, topk, N)
     x = dev(d["x"].view(np.int16)).view(torch.bfloat16)
-    wob.mxfp4_moe_gemm(x, dev(ids), dev(d["w_fp4"]), dev(d["w_scale"]), out=y)
+    wob.mxfp4_moe_gemm(x, dev(ids), dev(d["w_fp4"]), dev(d["w_scale"]), out=y, tile_m=tile_m)
     torch.cuda.synchronize()
     bits = host_bits(out)
     assert np.all(is_nan_bits(bits[0], wl.BF16)), "write before y"
@@ -53,30 +58,34 @@ def _check(oracle, d, ybits, ids=None):
     return y, yref
 
 
+@pytest.mark.parametrize("tile_m", TILE_M)
 @pytest.mark.parametrize("T,E,topk,N,K", [(64, 8, 2, 512, 256), (37, 4, 3, 400, 192),
                                           (200, 16, 4, 256, 2880), (5, 32, 4, 48, 64)])
-def test_moe_random_routing(wob, oracle, T, E, topk, N, K):
+def test_moe_random_routing(wob, oracle, T, E, topk, N, K, tile_m):
     d = wl.moe_inputs(T, E, topk, N, K, seed=T + N)
-    _check(oracle, d, _run(wob, d))
+    _check(oracle, d, _run(wob, d, tile_m=tile_m))
 
 
-@pytest.mark.parametrize("rows_per_expert", [16, 32, 64, 100, 256, 257])
-def test_moe_tile_heights(wob, oracle, rows_per_expert):
-    """Every expert gets exactly `rows_per_expert` rows (the page's tile heights
-    16/32/64, a ragged 100, one full 256-row tile and one row past it)."""
+@pytest.mark.parametrize("tile_m", TILE_M)
+@pytest.mark.parametrize("rows_per_expert", [16, 17, 32, 64, 100, 160, 161, 256, 257])
+def test_moe_tile_heights(wob, oracle, rows_per_expert, tile_m):
+    """Every expert gets exactly `rows_per_expert` rows (16/32/64 as on the page,
+    one row past a 16-row block, a ragged 100, a full 160-row expert tile and
+    one row past it, 256 and 257)."""
     E, topk = 4, 1
     T = E * rows_per_expert
     d = wl.moe_inputs(T, E, topk, 528, 320, seed=rows_per_expert)
     ids = (np.arange(T) % E).astype(np.int32).reshape(T, 1)
-    _check(oracle, d, _run(wob, d, ids), ids)
+    _check(oracle, d, _run(wob, d, ids, tile_m), ids)
 
 
-def test_moe_skewed_and_empty_experts(wob, oracle):
-    """All tokens on one expert (two 256-row tiles plus a tail) while the other
-    experts stay empty."""
+@pytest.mark.parametrize("tile_m", TILE_M)
+def test_moe_skewed_and_empty_experts(wob, oracle, tile_m):
+    """All tokens on one expert (several expert tiles plus a tail) while the
+    other experts stay empty."""
     d = wl.moe_inputs(600, 8, 1, 256, 128, seed=11)
     ids = np.full((600, 1), 5, np.int32)
-    _check(oracle, d, _run(wob, d, ids), ids)
+    _check(oracle, d, _run(wob, d, ids, tile_m), ids)
 
 
 def test_moe_top1_single_expert_is_dense(wob, oracle):
@@ -90,14 +99,15 @@ def test_moe_top1_single_expert_is_dense(wob, oracle):
     assert np.max(np.abs(y[:, 0, :] - ref)) <= 1e-3 + 1e-2 * np.max(np.abs(ref))
 
 
-def test_moe_out_of_range_ids_write_zero_rows(wob, oracle):
+@pytest.mark.parametrize("tile_m", TILE_M)
+def test_moe_out_of_range_ids_write_zero_rows(wob, oracle, tile_m):
     d = wl.moe_inputs(40, 6, 2, 304, 128, seed=7)
     ids = d["ids"].copy()
     ids[0, 0] = -1
     ids[3, 1] = 6
     ids[17, 0] = 1000
     ids[39, 1] = -2147483648
-    ybits = _run(wob, d, ids)
+    ybits = _run(wob, d, ids, tile_m)
     y, _ = _check(oracle, d, ybits, ids)
     for t, s in [(0, 0), (3, 1), (17, 0), (39, 1)]:
         assert np.all(ybits[t, s] == 0), (t, s)
@@ -139,13 +149,14 @@ def _moe_tile_samples(d, rng, width=128, per=4):
     return np.concatenate(ts), np.concatenate(ss), np.concatenate(ns)
 
 
-def test_config_moe_stage1_full_size(wob, oracle):
+@pytest.mark.parametrize("tile_m", TILE_M)
+def test_config_moe_stage1_full_size(wob, oracle, tile_m):
     """1024 tokens, 32 experts, top-4, K=2880, N=5760 in the benchmark's launch
-    configuration: every output finite, and for every expert and every
-    128-column block, four of its routed rows at four columns each (both
-    block edges) against the oracle."""
+    configuration (tile_m 32; 16 as well): every output finite, and for every
+    expert and every 128-column block, four of its routed rows at four columns
+    each (both block edges) against the oracle."""
     d = wl.BY_KEY["moe_stage1"].make()
-    ybits = _run(wob, d)
+    ybits = _run(wob, d, tile_m=tile_m)
     y = oracle.bf16_decode(ybits)
     assert np.all(np.isfinite(y))
     ts, ss, ns = _moe_tile_samples(d, np.random.default_rng(0))
@@ -157,7 +168,7 @@ def test_config_moe_stage1_full_size(wob, oracle):
 
 # --- fused stage-1 activation: silu(gate) * up -------------------------------------
 
-def _run_act(wob, d, ids=None):
+def _run_act(wob, d, ids=None, tile_m=32):
     torch = torch_mod()
     T, topk, N = d["T"], d["topk"], d["N"]
     ids = d["ids"] if ids is None else ids
@@ -166,45 +177,48 @@ def _run_act(wob, d, ids=None):
     y = out[1:T * topk + 1].view(T, topk, N // 2)
     x = dev(d["x"].view(np.int16)).view(torch.bfloat16)
     wob.mxfp4_moe_gemm(x, dev(ids), dev(d["w_fp4"]), dev(d["w_scale"]), out=y,
-                       act=wob.ACT_SILU_MUL)
+                       act=wob.ACT_SILU_MUL, tile_m=tile_m)
     torch.cuda.synchronize()
     bits = host_bits(out)
     assert np.all(is_nan_bits(bits[0], wl.BF16)) and np.all(is_nan_bits(bits[-1], wl.BF16))
     return bits[1:-1].reshape(T, topk, N // 2)
 
 
+@pytest.mark.parametrize("tile_m", TILE_M)
 @pytest.mark.parametrize("T,E,topk,N,K", [(64, 8, 2, 512, 256), (37, 4, 3, 416, 192),
                                           (200, 16, 4, 5760, 640), (5, 32, 4, 32, 64)])
-def test_moe_silu_mul_parity(wob, oracle, T, E, topk, N, K):
+def test_moe_silu_mul_parity(wob, oracle, T, E, topk, N, K, tile_m):
     d = wl.moe_inputs(T, E, topk, N, K, seed=T + N + 1)
     ids = d["ids"].copy()
     ids[0, 0] = -1  # out-of-range id: zero row
     pre = oracle.mxfp4_moe_gemm(d["x"], ids, d["w_fp4"], d["w_scale"], T, topk, E, N, K)
     ref = oracle.silu_mul(pre)
-    ybits = _run_act(wob, d, ids)
+    ybits = _run_act(wob, d, ids, tile_m)
     ok, err, bound = oracle.tolerance_ok(oracle.bf16_decode(ybits), ref)
     assert ok, f"max err {err} > bound {bound}"
     assert np.all(ybits[0, 0] == 0)
 
 
-@pytest.mark.parametrize("rows_per_expert", [16, 100, 257])
-def test_moe_silu_mul_tile_heights(wob, oracle, rows_per_expert):
+@pytest.mark.parametrize("tile_m", TILE_M)
+@pytest.mark.parametrize("rows_per_expert", [16, 17, 100, 161, 225, 257])
+def test_moe_silu_mul_tile_heights(wob, oracle, rows_per_expert, tile_m):
     E = 3
     T = E * rows_per_expert
     d = wl.moe_inputs(T, E, 1, 288, 320, seed=rows_per_expert + 5)
     ids = (np.arange(T) % E).astype(np.int32).reshape(T, 1)
     pre = oracle.mxfp4_moe_gemm(d["x"], ids, d["w_fp4"], d["w_scale"], T, 1, E, 288, 320)
-    ok, err, bound = oracle.tolerance_ok(oracle.bf16_decode(_run_act(wob, d, ids)),
+    ok, err, bound = oracle.tolerance_ok(oracle.bf16_decode(_run_act(wob, d, ids, tile_m)),
                                          oracle.silu_mul(pre))
     assert ok, f"max err {err} > bound {bound}"
 
 
-def test_config_moe_stage1_silu_mul_full_size(wob, oracle):
+@pytest.mark.parametrize("tile_m", TILE_M)
+def test_config_moe_stage1_silu_mul_full_size(wob, oracle, tile_m):
     """The full MoE shape with the fused activation: all outputs finite, 2000
     sampled outputs against the oracle's silu(gate) * up of sampled gate and
     up pre-activations."""
     d = wl.BY_KEY["moe_stage1"].make()
-    ybits = _run_act(wob, d)
+    ybits = _run_act(wob, d, tile_m=tile_m)
     y = oracle.bf16_decode(ybits)
     assert np.all(np.isfinite(y))
     rng = np.random.default_rng(1)

@@ -167,11 +167,14 @@ def moe_workspace_size(T: int, topk: int, E: int, N: int = 0, K: int = 0) -> int
     return int(_lib.lib().mxfp4_moe_gemm_workspace_size(T, topk, E, N, K))
 
 
-def mxfp4_moe_gemm(x, topk_ids, w_fp4, w_scale, out=None, workspace=None, act: int = ACT_NONE):
+def mxfp4_moe_gemm(x, topk_ids, w_fp4, w_scale, out=None, workspace=None, act: int = ACT_NONE,
+                   tile_m: int = 32):
     """MoE stage 1: x [T,K] bf16, topk_ids [T,topk] int32, w_fp4 [E,N,K/2] uint8 and
     w_scale [E,N,K/32] uint8 (E8M0) -> y [T,topk,N] bf16 (act=ACT_NONE) or
     y [T,topk,N/2] = silu(gate) * up (act=ACT_SILU_MUL).  workspace: device memory of
-    at least moe_workspace_size(T, topk, E, N, K) bytes (allocated when None)."""
+    at least moe_workspace_size(T, topk, E, N, K) bytes (allocated when None).
+    tile_m: 32 (the default, mxfp4_moe_gemm) or 16 (mxfp4_moe_gemm_tile_m), the
+    row padding of each expert's tile."""
     torch = _torch()
     if x.dim() != 2 or topk_ids.dim() != 2 or w_fp4.dim() != 3:
         raise ValueError("x must be [T, K], topk_ids [T, topk] and w_fp4 [E, N, K/2]")
@@ -186,6 +189,8 @@ def mxfp4_moe_gemm(x, topk_ids, w_fp4, w_scale, out=None, workspace=None, act: i
     _want(w_scale, "w_scale", (E, N, K // 32), (torch.uint8,))
     if act not in (ACT_NONE, ACT_SILU_MUL):
         raise ValueError(f"unknown activation {act}")
+    if tile_m not in (16, 32):
+        raise ValueError(f"tile_m={tile_m} must be 16 or 32")
     nout = N // 2 if act == ACT_SILU_MUL else N
     if out is None:
         out = torch.empty((T, topk, nout), dtype=torch.bfloat16, device=x.device)
@@ -198,9 +203,14 @@ def mxfp4_moe_gemm(x, topk_ids, w_fp4, w_scale, out=None, workspace=None, act: i
         raise ValueError(f"workspace holds {ws_bytes} bytes; {need} are needed")
     dev = _check_device(x, topk_ids, w_fp4, w_scale, out, workspace)
     with torch.cuda.device(dev):
-        st = _lib.lib().mxfp4_moe_gemm(
-            _ptr(x), _ptr(topk_ids), _ptr(w_fp4), _ptr(w_scale), _ptr(out), T, topk, E, N, K, act,
-            _ptr(workspace), ws_bytes, _stream(dev))
+        if tile_m == 32:
+            st = _lib.lib().mxfp4_moe_gemm(
+                _ptr(x), _ptr(topk_ids), _ptr(w_fp4), _ptr(w_scale), _ptr(out), T, topk, E, N, K,
+                act, _ptr(workspace), ws_bytes, _stream(dev))
+        else:
+            st = _lib.lib().mxfp4_moe_gemm_tile_m(
+                _ptr(x), _ptr(topk_ids), _ptr(w_fp4), _ptr(w_scale), _ptr(out), T, topk, E, N, K,
+                act, tile_m, _ptr(workspace), ws_bytes, _stream(dev))
     _lib.check(st, "mxfp4_moe_gemm")
     return out
 

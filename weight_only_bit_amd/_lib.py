@@ -20,7 +20,8 @@ ACT_NONE, ACT_SILU_MUL = 0, 1
 EXPORTS = [
     "wob_status_str", "wob_last_error", "wob_device_check",
     "w4a16_gemm", "w4a16_gemm_ex", "w4a16_gemm_grouped",
-    "mxfp4_moe_gemm_workspace_size", "mxfp4_moe_gemm", "mxfp4_moe_gemm_noalloc",
+    "mxfp4_moe_gemm_workspace_size", "mxfp4_moe_gemm", "mxfp4_moe_gemm_tile_m",
+    "mxfp4_moe_gemm_noalloc",
     "mxfp4_moe_stage2_workspace_size", "mxfp4_moe_stage2",
     "w4a16_dequant", "mxfp4_dequant", "wob_stream_read",
 ]
@@ -41,6 +42,8 @@ _SIGNATURES = {
     "mxfp4_moe_gemm_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "mxfp4_moe_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i, _vp, _sz,
                             _vp]),
+    "mxfp4_moe_gemm_tile_m": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i, _i,
+                                   _vp, _sz, _vp]),
     "mxfp4_moe_gemm_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i,
                                     _vp]),
     "mxfp4_moe_stage2_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),

@@ -293,10 +293,15 @@ int check_moe(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4, cons
 
 } // namespace
 
-int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
-                   const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E, int64_t N,
-                   int64_t K, int act, void *workspace, size_t workspace_bytes, void *stream)
+namespace {
+
+int moe_gemm_impl(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
+                  const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E, int64_t N,
+                  int64_t K, int act, int tile_m, void *workspace, size_t workspace_bytes,
+                  void *stream)
 {
+    if (tile_m != 16 && tile_m != 32)
+        return fail(WOB_INVALID_ARG, "tile_m %d is not 16 or 32", tile_m);
     bool noop;
     int s = check_moe(x, topk_ids, w_fp4, w_scale, y, T, topk, E, N, K, act, &noop);
     if (s != WOB_OK)
@@ -311,9 +316,28 @@ int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
     if (s != WOB_OK)
         return s;
     return launched(wob::launch_mxfp4_moe(x, topk_ids, w_fp4, w_scale, y, (int)T, (int)topk,
-                                          (int)E, (int)N, (int)K, act, workspace,
+                                          (int)E, (int)N, (int)K, act, tile_m, workspace,
                                           static_cast<hipStream_t>(stream)),
                     "mxfp4 moe");
+}
+
+} // namespace
+
+int mxfp4_moe_gemm(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
+                   const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E, int64_t N,
+                   int64_t K, int act, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return moe_gemm_impl(x, topk_ids, w_fp4, w_scale, y, T, topk, E, N, K, act, 32, workspace,
+                         workspace_bytes, stream);
+}
+
+int mxfp4_moe_gemm_tile_m(const void *x, const int32_t *topk_ids, const uint8_t *w_fp4,
+                          const uint8_t *w_scale, void *y, int64_t T, int64_t topk, int64_t E,
+                          int64_t N, int64_t K, int act, int tile_m, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    return moe_gemm_impl(x, topk_ids, w_fp4, w_scale, y, T, topk, E, N, K, act, tile_m,
+                         workspace, workspace_bytes, stream);
 }
 
 size_t mxfp4_moe_stage2_workspace_size(int64_t T, int64_t topk, int64_t E, int64_t H, int64_t I)
@@ -385,7 +409,7 @@ int mxfp4_moe_gemm_noalloc(const void *x, const int32_t *topk_ids, const uint8_t
     if (e != hipSuccess)
         return fail(WOB_HIP, "static scratch lookup: %s", hipGetErrorString(e));
     return launched(wob::launch_mxfp4_moe(x, topk_ids, w_fp4, w_scale, y, (int)T, (int)topk,
-                                          (int)E, (int)N, (int)K, act, scratch,
+                                          (int)E, (int)N, (int)K, act, 32, scratch,
                                           static_cast<hipStream_t>(stream)),
                     "mxfp4 moe (static scratch)");
 }

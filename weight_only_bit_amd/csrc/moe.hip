@@ -16,17 +16,24 @@
 //     tile) pair; its activation rows are gathered from x by token, the FP4
 //     words are expanded to bfloat16 with v_cvt_scalef32_pk_bf16_fp4 (one
 //     conversion per byte, two elements each, the E8M0 byte placed in the
-//     binary32 exponent as the scale), v_mfma_f32_32x32x16_bf16 multiplies,
-//     and the epilogue scatters rows to their pair index.  Stores are guarded
+//     binary32 exponent as the scale), v_mfma_f32_32x32x16_bf16 (or, with
+//     a 16-row tile height, v_mfma_f32_16x16x32_bf16) multiplies, and the
+//     epilogue scatters rows to their pair index.  Stores are guarded
 //     by the tile's row count and by N, so a tile that overhangs the weight
 //     rows (N not a multiple of the tile) never writes into neighbouring
 //     cells: the failure the page's store guard fixes.
 //
 // Tiles: 384 weight rows x up to 160 activation rows for the pre-activation
-// output, 256 x 256 for the fused activation (see moe_nb).  An expert's rows
-// form one tile when they fit (the average expert of a 1024-token, 32-expert,
-// top-4 batch has 128), so its weights stream from memory once; the tile
-// multiplies only the 32-row blocks its row count needs.
+// output, 256 x up to 224 (160 with 16-row blocks) for the fused activation
+// (see moe_nb).  An expert's rows form one tile when they fit (the average
+// expert of a 1024-token, 32-expert, top-4 batch has 128), so its weights
+// stream from memory once; the tile multiplies only the blocks its row count
+// needs, so an expert's rows are padded to a multiple of the tile height
+// (the MFMA block height): 32 rows by default, 16 on request.  Measured on
+// MI355X, the 16-row form is the slower one at every batch size tried (16 to
+// 1024 tokens: 4 to 16 %), although it pads less: its accumulators are four
+// times as many 4-register blocks, which the compiler shuffles between the
+// two register files inside the K loop.
 #include "wob_internal.hpp"
 #include "wob_tile.hpp"
 
@@ -40,23 +47,30 @@ static __device__ __align__(256) uint8_t moe_static_scratch[MOE_SCRATCH_BYTES];
 namespace wob {
 namespace {
 
-// Weight blocks per wave: 3 (384-row weight tiles, up to 160 activation
-// rows) for the pre-activation output, whose per-span fixed costs (barrier,
-// scale loads, code copies) then spread over 1.5x the MFMAs of a 256-row tile
-// at the ~128 rows of a typical expert; 2 (256 rows, up to 256 activation
-// rows) for the fused gate / up activation, which pairs weight blocks.
-template <bool ACT>
-constexpr int moe_nb() { return ACT ? 2 : 3; }
-// 32-row activation blocks per expert tile, at most: the fused-activation
-// tile stops at 7 (224 rows), since its 8-block form (the full 256 fp32
-// accumulator registers) spilled a register; a larger expert takes two tiles.
-template <bool ACT>
-constexpr int moe_mb_max() { return ACT ? 7 : TileGeo<moe_nb<ACT>()>::MB_MAX; }
-template <bool ACT>
-constexpr int moe_tm() { return 32 * moe_mb_max<ACT>(); } // rows per expert tile
-template <bool ACT>
-constexpr int moe_tn() { return TileGeo<moe_nb<ACT>()>::TN; } // weight rows per tile
-constexpr int MOE_TM_MIN = moe_tm<false>() < moe_tm<true>() ? moe_tm<false>() : moe_tm<true>();
+// Weight blocks per wave (tile height BR = MFMA block rows): 384-row weight
+// tiles (3 blocks of 32 or 6 of 16) for the pre-activation output, whose
+// per-span fixed costs (barrier, scale loads, code copies) then spread over
+// 1.5x the MFMAs of a 256-row tile at the ~128 rows of a typical expert;
+// 256 rows (128 gate rows and the matching 128 up rows) for the fused
+// gate / up activation, which pairs weight blocks.
+template <bool ACT, int BR>
+constexpr int moe_nb() { return (ACT ? 256 : 384) / (4 * BR); }
+template <bool ACT, int BR>
+using MoeGeo = TileGeo<moe_nb<ACT, BR>(), BR>;
+// Activation blocks per expert tile, at most: 160 rows (the 240 accumulator
+// registers of the 384-row tile); the fused-activation tile stops at 224
+// rows with 32-row blocks (its 256-row form spilled a register) and at 160
+// rows with 16-row blocks (more spilled); a larger expert takes two tiles.
+template <bool ACT, int BR>
+constexpr int moe_mb_max() { return (ACT && BR == 32) ? 7 : 160 / BR; }
+template <bool ACT, int BR>
+constexpr int moe_tm() { return BR * moe_mb_max<ACT, BR>(); } // rows per expert tile
+template <bool ACT, int BR>
+constexpr int moe_tn() { return MoeGeo<ACT, BR>::TN; } // weight rows per tile
+constexpr int MOE_TM_MIN = 160; // the smallest moe_tm of any variant
+static_assert(moe_tm<false, 32>() >= MOE_TM_MIN && moe_tm<true, 32>() >= MOE_TM_MIN &&
+                  moe_tm<false, 16>() >= MOE_TM_MIN && moe_tm<true, 16>() >= MOE_TM_MIN,
+              "workspace bound");
 constexpr int ROUTE_THREADS = 1024;
 
 struct MoeWs {
@@ -151,11 +165,11 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const int32_t 
 }
 
 // Gathered activation rows of one expert tile: row r is sorted pair
-// sorted[first + r], token pair / topk.  Offsets of this lane's DMA rows are
-// kept in registers for the whole tile.
-template <int MB>
+// sorted[first + r], token pair / topk.  Offsets of this lane's DMA rows
+// (NX = rows / 16 copies) are kept in registers for the whole tile.
+template <int NX>
 struct GatherRows {
-    uint32_t xo[2 * MB];
+    uint32_t xo[NX];
     const int32_t *pairs; // sorted + first
     uint16_t *base;       // y
     int ld;               // output row length
@@ -166,43 +180,45 @@ struct GatherRows {
 // The tile with MB 32-row blocks; ACT: the paired gate/up layout and the
 // fused silu(gate) * up store (I = N / 2 output columns), else the plain
 // pre-activation store.
-template <bool ACT, int MB>
-__device__ __forceinline__ void moe_run(const FmtFP4<ACT, moe_nb<ACT>()> &fmt, const int32_t *pairs,
-                                        int rows, int topk, const uint16_t *x, uint16_t *y, int K,
-                                        int N, int n0, uint8_t *smem, const TileLane &tl)
+template <bool ACT, int BR, int MB>
+__device__ __forceinline__ void moe_run(const FmtFP4<ACT, moe_nb<ACT, BR>(), BR> &fmt,
+                                        const int32_t *pairs, int rows, int topk,
+                                        const uint16_t *x, uint16_t *y, int K, int N, int n0,
+                                        uint8_t *smem, const TileLane<BR> &tl)
 {
-    GatherRows<MB> g;
+    constexpr int NX = BR * MB / 16;
+    GatherRows<NX> g;
     g.pairs = pairs;
     g.base = y;
     g.ld = ACT ? N / 2 : N;
 #pragma unroll
-    for (int i = 0; i < 2 * MB; ++i) {
+    for (int i = 0; i < NX; ++i) {
         const int p = pairs[min(16 * i + tl.rl, rows - 1)];
         g.xo[i] = (uint32_t)(p / topk) * (uint32_t)K * 2u;
     }
-    constexpr int NB = moe_nb<ACT>();
-    float16_t acc[NB][MB];
-    tile_mainloop<DT_BF16, NB, MB>(fmt, g, reinterpret_cast<const uint8_t *>(x), K, n0, N,
+    constexpr int NB = moe_nb<ACT, BR>();
+    typename AccT<BR>::type acc[NB][MB];
+    tile_mainloop<DT_BF16, NB, MB, BR>(fmt, g, reinterpret_cast<const uint8_t *>(x), K, n0, N,
                                        smem, tl, acc);
     if constexpr (ACT)
-        tile_store_silu_mul<DT_BF16, NB, MB>(acc, g, rows, n0, N / 2, tl, smem);
+        tile_store_silu_mul<DT_BF16, NB, MB, BR>(acc, g, rows, n0, N / 2, tl, smem);
     else
-        tile_store<DT_BF16, NB, MB>(acc, g, rows, n0, N, tl, smem);
+        tile_store<DT_BF16, NB, MB, BR>(acc, g, rows, n0, N, tl, smem);
 }
 
-template <bool ACT, int MB>
-__device__ __forceinline__ void moe_dispatch(int mb, const FmtFP4<ACT, moe_nb<ACT>()> &fmt,
+template <bool ACT, int BR, int MB>
+__device__ __forceinline__ void moe_dispatch(int mb, const FmtFP4<ACT, moe_nb<ACT, BR>(), BR> &fmt,
                                              const int32_t *pairs, int rows, int topk,
                                              const uint16_t *x, uint16_t *y, int K, int N, int n0,
-                                             uint8_t *smem, const TileLane &tl)
+                                             uint8_t *smem, const TileLane<BR> &tl)
 {
     if constexpr (MB > 1) {
         if (mb < MB) {
-            moe_dispatch<ACT, MB - 1>(mb, fmt, pairs, rows, topk, x, y, K, N, n0, smem, tl);
+            moe_dispatch<ACT, BR, MB - 1>(mb, fmt, pairs, rows, topk, x, y, K, N, n0, smem, tl);
             return;
         }
     }
-    moe_run<ACT, MB>(fmt, pairs, rows, topk, x, y, K, N, n0, smem, tl);
+    moe_run<ACT, BR, MB>(fmt, pairs, rows, topk, x, y, K, N, n0, smem, tl);
 }
 
 struct ZeroRows {
@@ -214,15 +230,15 @@ struct ZeroRows {
 
 // One (expert tile, weight-row tile) pair per workgroup.  ACT: tiles of 128
 // output columns (128 gate rows + the matching 128 up rows), else 384.
-template <bool ACT>
+template <bool ACT, int BR>
 __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ w_fp4,
     const uint8_t *__restrict__ w_scale, uint16_t *__restrict__ y, const int32_t *__restrict__ hdr,
     const int4 *__restrict__ tiles, const int32_t *__restrict__ sorted, int topk, int E, int N,
     int K, int n_nt, int nxcd)
 {
-    constexpr int NB = moe_nb<ACT>();
-    constexpr int TW = ACT ? moe_tn<ACT>() / 2 : moe_tn<ACT>(); // output columns per tile
+    constexpr int NB = moe_nb<ACT, BR>();
+    constexpr int TW = ACT ? moe_tn<ACT, BR>() / 2 : moe_tn<ACT, BR>(); // output columns per tile
     extern __shared__ __align__(16) uint8_t smem[];
     const int t = xcd_tile(hdr[0] * n_nt, nxcd);
     if (t < 0)
@@ -237,11 +253,11 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
         tile_store_zero<TW>(ZeroRows{pairs, y, Nout}, rows, n0, Nout);
         return;
     }
-    const TileLane tl;
-    const FmtFP4<ACT, NB> fmt(w_fp4 + (size_t)e * N * (K >> 1),
+    const TileLane<BR> tl;
+    const FmtFP4<ACT, NB, BR> fmt(w_fp4 + (size_t)e * N * (K >> 1),
                                   w_scale + (size_t)e * N * (K >> 5), N, K, n0, tl);
-    moe_dispatch<ACT, moe_mb_max<ACT>()>((rows + 31) >> 5, fmt, pairs, rows, topk, x, y, K, N,
-                                         n0, smem, tl);
+    moe_dispatch<ACT, BR, moe_mb_max<ACT, BR>()>((rows + BR - 1) / BR, fmt, pairs, rows, topk, x,
+                                                 y, K, N, n0, smem, tl);
 }
 
 // ---- Stage 2: down projection with the routing-weight combine ------------
@@ -256,27 +272,29 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_gemm_kernel(
 // order, so the result does not depend on timing.
 
 // A tile's rows of pre straight from the accumulators: the lane holds
-// D[n = 32 NB w + 32 nb + 8 g4 + 4 h + j][m = 32 mb + nl] in register 4 g4 + j
-// of block (nb, mb), i.e. four consecutive outputs of one row: one 16-byte
-// store each.  Rows past the tile's count and columns past H are not written.
-template <int NB, int MB>
-__device__ __forceinline__ void tile_store_rows_f32(const float16_t (&acc)[NB][MB], float *pre,
-                                                    const int32_t *pairs, int rows, int n0, int H,
-                                                    const TileLane &tl)
+// D[n = BR NB w + BR nb + 4 G g4 + 4 g + j][m = BR mb + nl] in register
+// 4 g4 + j of block (nb, mb), i.e. four consecutive outputs of one row: one
+// 16-byte store each.  Rows past the tile's count and columns past H are not
+// written.
+template <int NB, int MB, int BR>
+__device__ __forceinline__ void tile_store_rows_f32(const typename AccT<BR>::type (&acc)[NB][MB],
+                                                    float *pre, const int32_t *pairs, int rows,
+                                                    int n0, int H, const TileLane<BR> &tl)
 {
+    using GEO = TileGeo<NB, BR>;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        const int r = 32 * mb + tl.nl;
+        const int r = BR * mb + tl.nl;
         if (r >= rows)
             continue;
         float *row = pre + (size_t)pairs[r] * H;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int n = n0 + 32 * NB * tl.wave + 32 * nb + 8 * g4 + 4 * tl.h;
+            for (int g4 = 0; g4 < GEO::ACC / 4; ++g4) {
+                const int n = n0 + BR * NB * tl.wave + BR * nb + 4 * GEO::G * g4 + 4 * tl.g;
                 if (n < H) {
-                    const float16_t &v = acc[nb][mb];
+                    const auto &v = acc[nb][mb];
                     *reinterpret_cast<float4_t *>(row + n) =
                         float4_t{v[4 * g4 + 0], v[4 * g4 + 1], v[4 * g4 + 2], v[4 * g4 + 3]};
                 }
@@ -284,31 +302,39 @@ __device__ __forceinline__ void tile_store_rows_f32(const float16_t (&acc)[NB][M
     }
 }
 
-constexpr int MOE2_NB = 3; // 384-row weight tiles (2880 = 7.5 of them)
+// 384-row weight tiles of 32-row blocks, as stage 1 (measured on MI355X at
+// H = 2880: faster than 320-row tiles, which split the width evenly but make
+// 288 tiles for 32 experts, more than one round of the 256 compute units,
+// and faster than 16-row blocks).
+constexpr int MOE2_BR = 32;
+constexpr int MOE2_NB = 3;
+using Moe2Geo = TileGeo<MOE2_NB, MOE2_BR>;
 
 template <int MB>
-__device__ __forceinline__ void moe2_run(const FmtFP4<false, MOE2_NB> &fmt, const int32_t *pairs,
-                                         int rows, const uint16_t *a, float *pre, int I, int H,
-                                         int n0, uint8_t *smem, const TileLane &tl)
+__device__ __forceinline__ void moe2_run(const FmtFP4<false, MOE2_NB, MOE2_BR> &fmt,
+                                         const int32_t *pairs, int rows, const uint16_t *a,
+                                         float *pre, int I, int H, int n0, uint8_t *smem,
+                                         const TileLane<MOE2_BR> &tl)
 {
-    GatherRows<MB> g;
+    constexpr int NX = MOE2_BR * MB / 16;
+    GatherRows<NX> g;
     g.pairs = pairs;
     g.base = nullptr;
     g.ld = 0;
 #pragma unroll
-    for (int i = 0; i < 2 * MB; ++i)
+    for (int i = 0; i < NX; ++i)
         g.xo[i] = (uint32_t)pairs[min(16 * i + tl.rl, rows - 1)] * (uint32_t)I * 2u;
-    float16_t acc[MOE2_NB][MB];
-    tile_mainloop<DT_BF16, MOE2_NB, MB>(fmt, g, reinterpret_cast<const uint8_t *>(a), I, n0, H,
-                                        smem, tl, acc);
-    tile_store_rows_f32<MOE2_NB, MB>(acc, pre, pairs, rows, n0, H, tl);
+    typename AccT<MOE2_BR>::type acc[MOE2_NB][MB];
+    tile_mainloop<DT_BF16, MOE2_NB, MB, MOE2_BR>(fmt, g, reinterpret_cast<const uint8_t *>(a), I,
+                                                 n0, H, smem, tl, acc);
+    tile_store_rows_f32<MOE2_NB, MB, MOE2_BR>(acc, pre, pairs, rows, n0, H, tl);
 }
 
 template <int MB>
-__device__ __forceinline__ void moe2_dispatch(int mb, const FmtFP4<false, MOE2_NB> &fmt,
+__device__ __forceinline__ void moe2_dispatch(int mb, const FmtFP4<false, MOE2_NB, MOE2_BR> &fmt,
                                               const int32_t *pairs, int rows, const uint16_t *a,
                                               float *pre, int I, int H, int n0, uint8_t *smem,
-                                              const TileLane &tl)
+                                              const TileLane<MOE2_BR> &tl)
 {
     if constexpr (MB > 1) {
         if (mb < MB) {
@@ -326,7 +352,7 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_stage2_kernel(
     const int4 *__restrict__ tiles, const int32_t *__restrict__ sorted, int E, int H, int I,
     int n_nt, int nxcd)
 {
-    constexpr int TW = TileGeo<MOE2_NB>::TN;
+    constexpr int TW = Moe2Geo::TN;
     extern __shared__ __align__(16) uint8_t smem[];
     const int t = xcd_tile(hdr[0] * n_nt, nxcd);
     if (t < 0)
@@ -337,11 +363,11 @@ __global__ __launch_bounds__(TL_THREADS, 1) void moe_stage2_kernel(
     const int e = te.x, rows = te.z;
     if (e >= E)
         return; // ids outside [0, E): the combine skips these slots
-    const TileLane tl;
-    const FmtFP4<false, MOE2_NB> fmt(w_fp4 + (size_t)e * H * (I >> 1),
-                                     w_scale + (size_t)e * H * (I >> 5), H, I, n0, tl);
-    moe2_dispatch<moe_mb_max<false>()>((rows + 31) >> 5, fmt, sorted + te.y, rows, a, pre, I, H,
-                                       n0, smem, tl);
+    const TileLane<MOE2_BR> tl;
+    const FmtFP4<false, MOE2_NB, MOE2_BR> fmt(w_fp4 + (size_t)e * H * (I >> 1),
+                                              w_scale + (size_t)e * H * (I >> 5), H, I, n0, tl);
+    moe2_dispatch<moe_mb_max<false, MOE2_BR>()>((rows + MOE2_BR - 1) / MOE2_BR, fmt,
+                                                sorted + te.y, rows, a, pre, I, H, n0, smem, tl);
 }
 
 // y[t][h .. h+7] = sum over valid slots s (in order) of w[t][s] * pre[t*topk + s][h ..],
@@ -659,20 +685,19 @@ hipError_t launch_gemv_t(const void *x, const int32_t *ids, const uint8_t *w_fp4
     return launch_gemv<ACT, 1>(x, ids, w_fp4, w_scale, y, P, topk, E, N, K, stream);
 }
 
-template <bool ACT>
+template <bool ACT, int BR>
 hipError_t launch_gemm(const void *x, const uint8_t *w_fp4, const uint8_t *w_scale, void *y,
                        const MoeWs &w, int64_t P, int topk, int E, int N, int K,
                        hipStream_t stream)
 {
-    constexpr int NB = moe_nb<ACT>();
-    constexpr int LDS = TileGeo<NB>::lds_bytes(TileGeo<NB>::MB_MAX);
+    constexpr int LDS = MoeGeo<ACT, BR>::lds_bytes(moe_mb_max<ACT, BR>());
     static_assert(LDS <= 160 * 1024, "tile fits the LDS");
-    auto kern = moe_gemm_kernel<ACT>;
+    auto kern = moe_gemm_kernel<ACT, BR>;
     static std::atomic<uint64_t> lds_set{0};
     if (const hipError_t e = lds_optin(reinterpret_cast<const void *>(kern), LDS, lds_set);
         e != hipSuccess)
         return e;
-    const int tw = ACT ? moe_tn<ACT>() / 2 : moe_tn<ACT>();
+    const int tw = ACT ? moe_tn<ACT, BR>() / 2 : moe_tn<ACT, BR>();
     const int nout = ACT ? N / 2 : N;
     const int n_nt = (nout + tw - 1) / tw;
     const int nxcd = device_topology().xcds;
@@ -737,18 +762,20 @@ hipError_t launch_mxfp4_moe_stage2(const void *a, const int32_t *ids, const floa
                                            ((moe_workspace_bytes(T, topk, E) + 255) & ~(size_t)255));
     const size_t route_lds = (size_t)(3 * (E + 1)) * sizeof(int);
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(ROUTE_THREADS), route_lds, stream, ids,
-                       (int)P, E, moe_tm<false>(), ws.hdr, ws.tiles, ws.sorted);
+                       (int)P, E, moe_tm<false, MOE2_BR>(), ws.hdr, ws.tiles, ws.sorted);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    constexpr int LDS = TileGeo<MOE2_NB>::lds_bytes(TileGeo<MOE2_NB>::MB_MAX);
+    constexpr int MB2 = moe_mb_max<false, MOE2_BR>();
+    static_assert(MB2 <= Moe2Geo::MB_MAX, "routing tile fits the stage-2 tile");
+    constexpr int LDS = Moe2Geo::lds_bytes(MB2);
     static_assert(LDS <= 160 * 1024, "tile fits the LDS");
     static std::atomic<uint64_t> lds_set{0};
     if (const hipError_t e = lds_optin(reinterpret_cast<const void *>(moe_stage2_kernel), LDS,
                                        lds_set);
         e != hipSuccess)
         return e;
-    const int tw = TileGeo<MOE2_NB>::TN;
+    const int tw = Moe2Geo::TN;
     const int n_nt = (H + tw - 1) / tw;
     const int nxcd = device_topology().xcds;
     const int64_t grid = (int64_t)nxcd * (((int64_t)max_tiles(P, E) * n_nt + nxcd - 1) / nxcd);
@@ -777,7 +804,7 @@ size_t moe_workspace_bytes(int64_t T, int64_t topk, int64_t E)
 
 hipError_t launch_mxfp4_moe(const void *x, const int32_t *ids, const uint8_t *w_fp4,
                             const uint8_t *w_scale, void *y, int T, int topk, int E, int N, int K,
-                            int act, void *workspace, hipStream_t stream)
+                            int act, int tile_m, void *workspace, hipStream_t stream)
 {
     const int64_t P = (int64_t)T * topk;
     const int mrmax = mg_rows(K);
@@ -788,14 +815,19 @@ hipError_t launch_mxfp4_moe(const void *x, const int32_t *ids, const uint8_t *w_
                                           mrmax, stream);
     const MoeWs w = carve(workspace, P, E);
     const size_t route_lds = (size_t)(3 * (E + 1)) * sizeof(int);
-    const int tm = act ? moe_tm<true>() : moe_tm<false>();
+    const bool br16 = tile_m == 16;
+    const int tm = br16 ? (act ? moe_tm<true, 16>() : moe_tm<false, 16>())
+                        : (act ? moe_tm<true, 32>() : moe_tm<false, 32>());
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(ROUTE_THREADS), route_lds, stream, ids,
                        (int)P, E, tm, w.hdr, w.tiles, w.sorted);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    return act ? launch_gemm<true>(x, w_fp4, w_scale, y, w, P, topk, E, N, K, stream)
-               : launch_gemm<false>(x, w_fp4, w_scale, y, w, P, topk, E, N, K, stream);
+    if (br16)
+        return act ? launch_gemm<true, 16>(x, w_fp4, w_scale, y, w, P, topk, E, N, K, stream)
+                   : launch_gemm<false, 16>(x, w_fp4, w_scale, y, w, P, topk, E, N, K, stream);
+    return act ? launch_gemm<true, 32>(x, w_fp4, w_scale, y, w, P, topk, E, N, K, stream)
+               : launch_gemm<false, 32>(x, w_fp4, w_scale, y, w, P, topk, E, N, K, stream);
 }
 
 } // namespace wob

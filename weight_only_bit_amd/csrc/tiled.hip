@@ -119,18 +119,18 @@ __device__ bool grouped_tile(const int64_t *off, int G, int total_M, int TM, int
 
 template <int DT, int NB, int MB, class Fmt>
 __device__ __forceinline__ void run_tile(const Fmt &fmt, const ContigRows &rws, const uint8_t *xbase,
-                                         int K, int N, int n0, uint8_t *smem, const TileLane &tl)
+                                         int K, int N, int n0, uint8_t *smem, const TileLane<> &tl)
 {
     float16_t acc[NB][MB];
-    tile_mainloop<DT, NB, MB>(fmt, rws, xbase, K, n0, N, smem, tl, acc);
-    tile_store<DT, NB, MB>(acc, rws, rws.rows, n0, N, tl, smem);
+    tile_mainloop<DT, NB, MB, 32>(fmt, rws, xbase, K, n0, N, smem, tl, acc);
+    tile_store<DT, NB, MB, 32>(acc, rws, rws.rows, n0, N, tl, smem);
 }
 
 // Runs the tile with the smallest block count that covers `rows`.
 template <int DT, int NB, int MB, class Fmt>
 __device__ __forceinline__ void dispatch_tile(int mb, const Fmt &fmt, const ContigRows &rws,
                                               const uint8_t *xbase, int K, int N, int n0,
-                                              uint8_t *smem, const TileLane &tl)
+                                              uint8_t *smem, const TileLane<> &tl)
 {
     if constexpr (MB > 1) {
         if (mb < MB) {
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
         return;
     const int n0 = nt * GEO::TN;
     const int G = K >> (5 + gshift);
-    const TileLane tl;
+    const TileLane<> tl;
     const FmtW4<DT, HAS_Z, NB, GW> fmt(qweight + (size_t)e * N * (K >> 3),
                                    scales + (size_t)e * N * G,
                                    HAS_Z ? qzeros + (size_t)e * (N >> 3) * G : qzeros, N, K,

@@ -69,9 +69,10 @@ hipError_t launch_mxfp4_moe_stage2(const void *a, const int32_t *ids, const floa
 // and its address on the current device (looked up on first use per device).
 size_t moe_scratch_bytes();
 hipError_t moe_scratch(void **ptr);
+// tile_m: 32 or 16 (MFMA block height of the expert tiles; T <= 8 ignores it).
 hipError_t launch_mxfp4_moe(const void *x, const int32_t *ids, const uint8_t *w_fp4,
                             const uint8_t *w_scale, void *y, int T, int topk, int E, int N, int K,
-                            int act, void *workspace, hipStream_t stream);
+                            int act, int tile_m, void *workspace, hipStream_t stream);
 
 // Dequantization probes.
 hipError_t launch_w4a16_dequant(const uint32_t *qweight, const void *scales, const uint32_t *qzeros,

@@ -13,24 +13,32 @@
 // WMMA path", section Cause), here registers -> MFMA operands.
 //
 // gfx950 realisation:
-//  * Matrix core: v_mfma_f32_32x32x16_{f16,bf16} (32 cycles each, measured
-//    with the MFMA busy counter), so every tile is built from 32 x 32 blocks.
-//  * 4 waves; wave w owns weight rows n0 + 32 NB w .. +32 NB - 1 (NB 32-row
-//    blocks nb) and all TM = 32 MB activation rows of the tile: NB x MB
-//    accumulator blocks of 16 fp32 registers (NB * MB <= 16, so the
-//    accumulators take at most 256 of a lane's 512 registers).  TN = 128 NB.
+//  * Matrix core: blocks of BR x BR outputs, BR = 32 with
+//    v_mfma_f32_32x32x16_{f16,bf16} (32 busy cycles each, measured with the
+//    MFMA busy counter) or BR = 16 with v_mfma_f32_16x16x32_{f16,bf16} (16
+//    cycles for half the products: the same rate).  Both forms cost the same
+//    dequantization and LDS reads per product; BR = 16 halves the row
+//    granularity of a tile (the grouped and MoE forms pad a group's rows to
+//    whole blocks).
+//  * 4 waves; wave w owns weight rows n0 + BR NB w .. +BR NB - 1 (NB BR-row
+//    blocks nb) and all TM = BR MB activation rows of the tile: NB x MB
+//    accumulator blocks of BR^2 / 64 fp32 registers (at most 256 of a lane's
+//    512 registers in all).  TN = 4 BR NB.
 //    One activation operand read from LDS feeds NB MFMAs and one dequantized
 //    weight word feeds MB, so NB trades LDS reads for dequantization work.
 //    Measured on MI355X, the dequantization weighs more: NB = 2 (256 x 256)
-//    for W4A16; NB = 3 (384 x 160) for MoE experts of ~128 rows; NB = 4
-//    (512 x 128) was slower for both, although it moves the fewest bytes into
-//    LDS per MFMA (2 TM + TN / 2 bytes per k is smallest at TN = 4 TM).
-//  * K advances in spans of 128 (8 MFMA steps of 16).  Lane (nl, h) =
-//    (lane % 32, lane / 32) takes 32 bytes of weight row nl of each block:
-//    words 8h .. 8h+7 of the span, i.e. k = 64h .. 64h+63 of the span, as two
-//    16-byte halves hf (32 k each).  MFMA step s uses word s of that load:
-//    operand slot (h, e) holds k = 64h + 8s + e.  The activation operand uses
-//    the same slots, so the pairing of k values is the same on both sides.
+//    for W4A16; 384 weight rows for MoE experts of ~128 rows; 512 x 128 was
+//    slower for both, although it moves the fewest bytes into LDS per MFMA
+//    (2 TM + TN / 2 bytes per k is smallest at TN = 4 TM).
+//  * K advances in spans of 128.  The G = 64 / BR lane groups g = lane / BR
+//    split the span's k: lane (nl, g) = (lane % BR, lane / BR) takes the
+//    128 / G k of group g of weight row nl of each block, i.e. PPL = 4 / G
+//    16-byte pieces hf (32 k each): words 4 PPL g .. 4 PPL g + 4 PPL - 1 of
+//    the row's span.  The span takes NS = 4 PPL MFMA steps; step s uses word
+//    s of the lane's pieces: operand slot (g, e) holds k = (128 / G) g + 8 s
+//    + e (BR = 32: 64 h + 8 s + e over 8 steps of 16 k; BR = 16: 32 g + 8 s
+//    + e over 4 steps of 32 k).  The activation operand uses the same slots,
+//    so the pairing of k values is the same on both sides.
 //  * The activation tile (TM rows x 128 k, 256 bytes per row) is copied from
 //    global memory straight into LDS with global_load_lds_dwordx4 (no staging
 //    registers), double buffered across spans.  Within a row the 16-byte block
@@ -43,19 +51,19 @@
 //    instruction reads sixteen contiguous 64-byte row segments instead of
 //    scattering 16-byte pieces of 32 rows (measured: the scattered per-lane
 //    code loads cost more than a fifth of the kernel).  A lane reads back its
-//    NB rows' 32 bytes per span with 2 NB ds_read_b128; LDS row R keeps its
-//    16-byte piece p at position p ^ ((R >> 2) & 3), which makes those reads
+//    NB rows' pieces with PPL NB ds_read_b128; LDS row R keeps its 16-byte
+//    piece p at position p ^ ((R >> 2) & 3), which makes those reads
 //    bank-conflict free.
-//  * Software pipeline: within a span the loop runs over the 8 MFMA steps;
+//  * Software pipeline: within a span the loop runs over the NS MFMA steps;
 //    each step dequantizes the NB weight words it needs (one per 32-row
 //    block) and issues its NB x MB MFMAs, while the next step's activation
 //    operands are read from LDS and its words are dequantized.  The per-row
 //    scales and zero-points are double buffered in registers and loaded a
 //    whole span ahead; the next span's activation and code tiles stream into
-//    the other LDS buffers.  Those copies are spread over the first five
-//    steps, a few per step (measured: issued in one burst at the start of the
-//    span they stalled the wave for a fifth of the loop), with scalar LDS
-//    addresses and one vector add per copy.
+//    the other LDS buffers.  Those copies are spread over the first steps
+//    of the span, a few per step (measured: issued in one burst at the start
+//    of the span they stalled the wave for a fifth of the loop), with scalar
+//    LDS addresses and one vector add per copy.
 //  * Tails: weight rows past the matrix are clamped to valid addresses and
 //    never stored; activation rows past the tile's row count are clamped to a
 //    valid row and never stored; a 32-wide K slice past K gets zero weights.
@@ -64,11 +72,12 @@
 // policy with:
 //    const uint8_t *wq;                   codes of row 0 of the matrix
 //    int tile_row(int n0, int N, int t) const;  matrix row of tile row t (clamped)
-//    (the policy is built for one NB and addresses rows 32 NB w + 32 nb + nl)
+//    (the policy is built for one NB and BR and addresses rows
+//    BR NB w + BR nb + nl)
 //    struct Meta;                         a lane's scales / zero-points of a span
 //    static constexpr int NLOADS;         vector-memory operations per load_meta()
 //    void load_meta(int span, Meta &m) const;
-//    void zero_past_k(int span, u32x4 (&cw)[NB][2], Meta &m) const;
+//    void zero_past_k(int span, u32x4 (&cw)[NB][PPL], Meta &m) const;
 //                                         weights of slices past K -> 0 (codes or scales)
 //    u32x4 dequant(uint32_t word, const Meta &m, int nb, int st) const;
 #pragma once
@@ -85,23 +94,35 @@ constexpr int TL_THREADS = 64 * TL_WAVES;
 constexpr int TL_SPAN = 128; // K per span
 constexpr int TL_ROWB = 256; // LDS bytes per activation row of a span
 
-// Tile geometry for NB weight blocks per wave.
-template <int NB>
+// Tile geometry for NB weight blocks of BR rows per wave.
+template <int NB, int BR = 32>
 struct TileGeo {
-    static_assert(NB >= 2 && NB <= 4, "weight blocks per wave");
-    static constexpr int TN = 32 * NB * TL_WAVES; // weight rows per tile
-    static constexpr int MB_MAX = 16 / NB;        // activation blocks per tile, at most
-    static constexpr int TM_MAX = 32 * MB_MAX;
-    static constexpr int WBUF = TN * 64;          // LDS bytes of one span's code tile
-    static constexpr int WDMA = TN / 64;          // code copies per wave per span
-    // LDS bytes of a tile with mb 32-row blocks: two span buffers of each
+    static_assert(BR == 32 || BR == 16, "MFMA block height");
+    static_assert(NB >= 2 && NB * BR <= 128, "weight blocks per wave");
+    static constexpr int G = 64 / BR;               // lane groups splitting a span's k
+    static constexpr int PPL = 4 / G;               // 16-byte code pieces per lane per span
+    static constexpr int NS = 4 * PPL;              // MFMA steps per span
+    static constexpr int ACC = BR * BR / 64;        // accumulator registers per block
+    static constexpr int TN = BR * NB * TL_WAVES;   // weight rows per tile
+    static constexpr int MB_MAX = 256 / (NB * ACC); // activation blocks per tile, at most
+    static constexpr int TM_MAX = BR * MB_MAX;
+    static constexpr int WBUF = TN * 64;            // LDS bytes of one span's code tile
+    static constexpr int WDMA = TN / 64;            // code copies per wave per span
+    static_assert(TN % 64 == 0, "whole code copies");
+    // LDS bytes of a tile with mb BR-row blocks: two span buffers of each
     // operand, or the epilogue's staging of the output tile if larger.
     __host__ __device__ static constexpr int lds_bytes(int mb)
     {
-        const int main = 2 * 32 * mb * TL_ROWB + 2 * WBUF;
-        const int stage = 32 * mb * (2 * TN + 16 + 4); // staged rows + row-index table
+        const int main = 2 * BR * mb * TL_ROWB + 2 * WBUF;
+        const int stage = BR * mb * (2 * TN + 16 + 4); // staged rows + row-index table
         return main > stage ? main : stage;
     }
+};
+
+// Accumulator block of BR x BR outputs: BR^2 / 64 fp32 registers per lane.
+template <int BR>
+struct AccT {
+    typedef float type __attribute__((ext_vector_type(BR * BR / 64)));
 };
 
 // s_waitcnt that waits until at most `n` vector-memory operations are
@@ -149,26 +170,41 @@ __device__ __forceinline__ void lds_dma16(const void *sbase_any, uint32_t voff, 
                  : "memory");
 }
 
-template <int DT>
-__device__ __forceinline__ float16_t mfma32x32x16(const u32x4 &a, const u32x4 &b, const float16_t &c)
+// One MFMA of a BR x BR block: A = 8 weight values of row nl (slot g), B = 8
+// activation values of row nl (slot g), D[weight row][activation row].
+template <int DT, int BR>
+__device__ __forceinline__ typename AccT<BR>::type mfma_blk(const u32x4 &a, const u32x4 &b,
+                                                            const typename AccT<BR>::type &c)
 {
-    if constexpr (DT == DT_F16)
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<half8_t>(a), bitcast<half8_t>(b), c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf168_t>(a), bitcast<bf168_t>(b), c, 0, 0, 0);
+    if constexpr (BR == 32) {
+        if constexpr (DT == DT_F16)
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<half8_t>(a), bitcast<half8_t>(b),
+                                                          c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf168_t>(a),
+                                                           bitcast<bf168_t>(b), c, 0, 0, 0);
+    } else {
+        if constexpr (DT == DT_F16)
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(a), bitcast<half8_t>(b),
+                                                          c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf168_t>(a),
+                                                           bitcast<bf168_t>(b), c, 0, 0, 0);
+    }
 }
 
 // Lane coordinates inside the tile.
+template <int BR = 32>
 struct TileLane {
-    int wave, lane, nl, h;
+    int wave, lane, nl, g;
     int rl;   // activation row (mod 16) this lane copies in every DMA instruction
     int xblk; // 16-byte block of that row this lane copies
     __device__ TileLane()
     {
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // uniform: scalar LDS addresses
         lane = threadIdx.x & 63;
-        nl = lane & 31;
-        h = lane >> 5;
+        nl = lane & (BR - 1);
+        g = lane / BR;
         rl = 4 * wave + (lane >> 4);
         xblk = (lane & 15) ^ rl;
     }
@@ -179,19 +215,22 @@ struct TileLane {
 // tile, already clamped to a valid row:  uint32_t XRows::off(int i) const
 // returns the offset of row 16 i + rl for this lane.
 //
-// The tile body: runs the whole K loop for one (128 NB) x (32 MB) tile and
+// The tile body: runs the whole K loop for one (4 BR NB) x (BR MB) tile and
 // leaves the accumulators in `acc`.  `Fmt` holds this lane's weight
 // addressing.
-template <int DT, int NB, int MB, class Fmt, class XRows>
+template <int DT, int NB, int MB, int BR, class Fmt, class XRows>
 __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
                                               const uint8_t *xbase, int K, int n0, int N,
-                                              uint8_t *smem, const TileLane &tl,
-                                              float16_t (&acc)[NB][MB])
+                                              uint8_t *smem, const TileLane<BR> &tl,
+                                              typename AccT<BR>::type (&acc)[NB][MB])
 {
-    using GEO = TileGeo<NB>;
+    using GEO = TileGeo<NB, BR>;
     static_assert(MB >= 1 && MB <= GEO::MB_MAX, "accumulator budget");
-    constexpr int TM = 32 * MB;
+    constexpr int TM = BR * MB;
+    static_assert(TM % 16 == 0, "whole activation copies");
     constexpr int WD = GEO::WDMA;
+    constexpr int PPL = GEO::PPL;
+    constexpr int NS = GEO::NS;
     const int S = (K + TL_SPAN - 1) / TL_SPAN;
     const uint32_t lds0 = (uint32_t)(size_t)(lds_ptr_t *)smem;
     const uint32_t wlds0 = lds0 + (uint32_t)(2 * TM * TL_ROWB);
@@ -216,9 +255,9 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
     // (L % 16) ^ rl of that row.  Blocks past K are clamped inside the row
     // (they meet zero weights).
     //
-    // Copy d of a span (d < 2 MB: activation instruction d, else code
-    // instruction d - 2 MB).  The per-span lane offsets kx / kw are computed
-    // once per span; LDS addresses are wave-uniform (scalar).
+    // Copy d of a span (d < TM / 16: activation instruction d, else code
+    // instruction d - TM / 16).  The per-span lane offsets kx / kw are
+    // computed once per span; LDS addresses are wave-uniform (scalar).
     constexpr int ND = TM / 16 + WD;
     auto dma = [&](int d, int buf, uint32_t kx, uint32_t kw) __attribute__((always_inline)) {
         if (d < TM / 16) {
@@ -241,7 +280,7 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
+            for (int e = 0; e < GEO::ACC; ++e)
                 acc[nb][mb][e] = 0.f;
 
     // Scales / zero-points double buffered: mA / mB alternate between "this
@@ -259,13 +298,13 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
     __builtin_amdgcn_s_waitcnt(0);
     barrier_only();
 
-    // MFMAs of one step in GR groups; with group g of step st goes copy
-    // GR st + g of the next span (all ND copies land in the first five
-    // steps), so the copies are spread over the span instead of issued in one
-    // burst.
+    // BR = 32: MFMAs of one step in GR groups; with group g of step st goes
+    // copy GR st + g of the next span (all copies land in the first five of
+    // the eight steps at the largest tiles), so the copies are spread over
+    // the span instead of issued in one burst.
     constexpr int NM = NB * MB;
     constexpr int GR = NM < 4 ? NM : 4; // group g: MFMAs [g NM / GR, (g + 1) NM / GR)
-    static_assert(ND <= 8 * GR, "every copy of the next span gets a slot");
+    static_assert(BR != 32 || ND <= NS * GR, "every copy of the next span gets a slot");
 
     // One span: MFMAs on LDS buffers span & 1 with the scales in `cur`.  At
     // entry the next span's scales (the other buffer) have landed or are in
@@ -277,78 +316,155 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
         uint32_t kx, kw;
         koff(min(span + 1, S - 1), kx, kw);
         const uint8_t *xb = smem + (size_t)buf * TM * TL_ROWB;
-        // This lane's packed codes of the span: rows 32 NB w + 32 nb + nl,
-        // pieces 2 h + hf (k = 64 h + 32 hf .. +31 of the span).
+        // This lane's packed codes of the span: rows BR NB w + BR nb + nl,
+        // pieces PPL g + hf (k = 32 (PPL g + hf) .. +31 of the span).
         const uint8_t *wb = wsm + buf * GEO::WBUF;
-        u32x4 cw[NB][2];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int R = 32 * NB * tl.wave + 32 * nb + tl.nl;
-                const int pos = (2 * tl.h + hf) ^ ((tl.nl >> 2) & 3);
-                cw[nb][hf] = *reinterpret_cast<const u32x4 *>(wb + R * 64 + 16 * pos);
-            }
-        // Only a span that crosses K (uniform test) has slices past K; the
-        // format zeroes their weights once (codes or scales).
-        if (span * TL_SPAN + TL_SPAN > K)
-            fmt.zero_past_k(span, cw, cur);
-        // Activation operand of block mb, step st: 32 rows (nl), 16-byte
-        // block 8h + st of the span.
+        // Activation operand of block mb, step st: BR rows (nl), 16-byte
+        // block NS g + st of the span.
         auto read_x = [&](int mb, int st) __attribute__((always_inline)) {
-            const int R = 32 * mb + tl.nl;
-            const int p = (8 * tl.h + st) ^ (R & 15);
+            const int R = BR * mb + tl.nl;
+            const int p = (NS * tl.g + st) ^ (R & 15);
             return *reinterpret_cast<const u32x4 *>(xb + R * TL_ROWB + 16 * p);
         };
-        auto dq = [&](int nb, int st) __attribute__((always_inline)) {
-            return fmt.dequant(cw[nb][st >> 2][st & 3], cur, nb, st);
-        };
-        u32x4 wc[NB], wn[NB], xc[MB], xn[MB];
+        if constexpr (BR == 32) {
+            u32x4 cw[NB][PPL];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            wc[nb] = dq(nb, 0);
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            xc[mb] = read_x(mb, 0);
+                for (int hf = 0; hf < PPL; ++hf) {
+                    const int R = BR * NB * tl.wave + BR * nb + tl.nl;
+                    const int pos = (PPL * tl.g + hf) ^ ((tl.nl >> 2) & 3);
+                    cw[nb][hf] = *reinterpret_cast<const u32x4 *>(wb + R * 64 + 16 * pos);
+                }
+            // Only a span that crosses K (uniform test) has slices past K;
+            // the format zeroes their weights once (codes or scales).
+            if (span * TL_SPAN + TL_SPAN > K)
+                fmt.zero_past_k(span, cw, cur);
+            auto dq = [&](int nb, int st) __attribute__((always_inline)) {
+                return fmt.dequant(cw[nb][st >> 2][st & 3], cur, nb, st);
+            };
+            u32x4 wc[NB], wn[NB], xc[MB], xn[MB];
+    #pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                wc[nb] = dq(nb, 0);
+    #pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                xc[mb] = read_x(mb, 0);
+    #pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                if (st < NS - 1) {
+    #pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        xn[mb] = read_x(mb, st + 1);
+    #pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        wn[nb] = dq(nb, st + 1);
+                }
+    #pragma unroll
+                for (int g = 0; g < GR; ++g) {
+    #pragma unroll
+                    for (int j = g * NM / GR; j < (g + 1) * NM / GR; ++j)
+                        acc[j % NB][j / NB] =
+                            mfma_blk<DT, BR>(wc[j % NB], xc[j / NB], acc[j % NB][j / NB]);
+                    if (GR * st + g < ND)
+                        dma(GR * st + g, buf ^ 1, kx, kw);
+                }
+                // Issue order inside the step: every MFMA followed by two of the
+                // next step's dequantization ops and, every second MFMA, one of its
+                // LDS operand reads (measured: the compiler's own order clustered
+                // up to a dozen VALU ops between two MFMAs; this order was ~1 %
+                // faster on the prefill shape).
+    #pragma unroll
+                for (int j = 0; j < NM; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0); // two VALU
+                    if (j % 2 == 1)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // one LDS read
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (st < NS - 1) {
+    #pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        wc[nb] = wn[nb];
+    #pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        xc[mb] = xn[mb];
+                }
+            }
+        } else {
+            // BR = 16: the step's MB activation operands would double the
+            // registers of the BR = 32 form, so they stream through a ring of
+            // XR operands instead, read LA positions ahead along the flattened
+            // order q = MB st + mb (LA = 4 measured fastest of 2 and 4); the
+            // next step's weight words are dequantized across the step's
+            // positions, and the copies of the next span go out over the
+            // first half of the span.
+            constexpr int LA = 4, XR = LA + 1;
+            constexpr int NQ = NS * MB;
+            constexpr int HALF = NQ / 2 > 0 ? NQ / 2 : 1;
+            // The lane's single piece per block is read one 4-byte word (one
+            // step) at a time, a step ahead of its dequantization, so only
+            // NB code words are live instead of NB pieces.  Slices past K:
+            // zero codes (a per-lane mask) or zero scales, as the format says.
+            static_assert(PPL == 1, "one piece per lane");
+            if (span * TL_SPAN + TL_SPAN > K) {
+                if constexpr (!Fmt::ZERO_CODES) {
+                    u32x4 none[NB][PPL];
+                    fmt.zero_past_k(span, none, cur);
+                }
+            }
+            const uint32_t cmask =
+                (Fmt::ZERO_CODES && span * TL_SPAN + 32 * tl.g >= K) ? 0u : ~0u;
+            const uint8_t *wl =
+                wb + (BR * NB * tl.wave + tl.nl) * 64 + 16 * (tl.g ^ ((tl.nl >> 2) & 3));
+            auto word = [&](int nb, int st) __attribute__((always_inline)) {
+                return *reinterpret_cast<const uint32_t *>(wl + BR * nb * 64 + 4 * st) & cmask;
+            };
+            uint32_t cn[NB];
+            u32x4 wc[NB], wn[NB], xr[XR];
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            if (st < 7) {
+            for (int nb = 0; nb < NB; ++nb) {
+                wc[nb] = fmt.dequant(word(nb, 0), cur, nb, 0);
+                cn[nb] = word(nb, 1);
+            }
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    xn[mb] = read_x(mb, st + 1);
+            for (int q = 0; q < LA && q < NQ; ++q)
+                xr[q % XR] = read_x(q % MB, q / MB);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int st = q / MB, mb = q % MB;
+                if (q + LA < NQ)
+                    xr[(q + LA) % XR] = read_x((q + LA) % MB, (q + LA) / MB);
+                if (st < NS - 1) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        if (nb * MB / NB == mb) {
+                            wn[nb] = fmt.dequant(cn[nb], cur, nb, st + 1);
+                            if (st + 2 < NS)
+                                cn[nb] = word(nb, st + 2);
+                        }
+                }
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    wn[nb] = dq(nb, st + 1);
-            }
+                    acc[nb][mb] = mfma_blk<DT, BR>(wc[nb], xr[q % XR], acc[nb][mb]);
 #pragma unroll
-            for (int g = 0; g < GR; ++g) {
+                for (int d = 0; d < ND; ++d)
+                    if (d * HALF / ND == q)
+                        dma(d, buf ^ 1, kx, kw);
 #pragma unroll
-                for (int j = g * NM / GR; j < (g + 1) * NM / GR; ++j)
-                    acc[j % NB][j / NB] =
-                        mfma32x32x16<DT>(wc[j % NB], xc[j / NB], acc[j % NB][j / NB]);
-                if (GR * st + g < ND)
-                    dma(GR * st + g, buf ^ 1, kx, kw);
-            }
-            // Issue order inside the step: every MFMA followed by two of the
-            // next step's dequantization ops and, every second MFMA, one of its
-            // LDS operand reads (measured: the compiler's own order clustered
-            // up to a dozen VALU ops between two MFMAs; this order was ~1 %
-            // faster on the prefill shape).
+                for (int nb = 0; nb < NB; ++nb) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 1, 0); // one VALU
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // one LDS read
+                if (mb == MB - 1) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (st < NS - 1) {
 #pragma unroll
-            for (int j = 0; j < NM; ++j) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0); // two VALU
-                if (j % 2 == 1)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // one LDS read
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if (st < 7) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    wc[nb] = wn[nb];
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    xc[mb] = xn[mb];
+                        for (int nb = 0; nb < NB; ++nb)
+                            wc[nb] = wn[nb];
+                    }
+                }
             }
         }
         // `cur` is consumed: refill it for span + 2 (clamped, so the wait
@@ -375,42 +491,44 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
 // Store one tile's accumulators through LDS, so that every global store
 // instruction writes whole 512-byte row segments of y (measured: storing the
 // accumulator layout directly, 8 bytes per lane across 32 rows, took about a
-// twelfth of the prefill kernel).  Lane holds D[n = 8 g4 + 4 h + j][m = nl] of
-// block (nb, mb) in register 4 g4 + j; the tile is staged as TM rows of 256
-// activation-dtype values (row stride padded by 16 bytes against bank
-// conflicts) in the LDS the main loop has released.  The output rows:
-// yr.base + yr.index(r) * yr.ld for tile row r < rows; the indices are read
-// once into LDS (for gathered MoE rows each is a global load, which the copy
-// loop would otherwise repeat for every 16-byte chunk).
-template <int DT, int MB, class YRows>
+// twelfth of the prefill kernel).  Lane (nl, g) holds D[n = 4 G g4 + 4 g +
+// j][m = nl] of block (nb, mb) in register 4 g4 + j (G = 64 / BR lane groups;
+// BR = 32: n = 8 g4 + 4 g + j, g4 < 4; BR = 16: n = 4 g + j); the tile is
+// staged as TM rows of TN activation-dtype values (row stride padded by 16
+// bytes against bank conflicts) in the LDS the main loop has released.  The
+// output rows: yr.base + yr.index(r) * yr.ld for tile row r < rows; the
+// indices are read once into LDS (for gathered MoE rows each is a global
+// load, which the copy loop would otherwise repeat for every 16-byte chunk).
+template <int TM, class YRows>
 __device__ __forceinline__ uint32_t *stage_row_index(const YRows &yr, int rows, uint8_t *tbl_lds)
 {
     uint32_t *tbl = reinterpret_cast<uint32_t *>(tbl_lds);
-    static_assert(32 * MB <= TL_THREADS, "one row index per thread");
+    static_assert(TM <= TL_THREADS, "one row index per thread");
     if ((int)threadIdx.x < rows)
         tbl[threadIdx.x] = yr.index(threadIdx.x);
     return tbl;
 }
 
-template <int DT, int NB, int MB, class YRows>
-__device__ __forceinline__ void tile_store(const float16_t (&acc)[NB][MB], const YRows &yr,
-                                          int rows, int n0, int N, const TileLane &tl,
-                                          uint8_t *smem)
+template <int DT, int NB, int MB, int BR, class YRows>
+__device__ __forceinline__ void tile_store(const typename AccT<BR>::type (&acc)[NB][MB],
+                                          const YRows &yr, int rows, int n0, int N,
+                                          const TileLane<BR> &tl, uint8_t *smem)
 {
-    constexpr int TN = TileGeo<NB>::TN;
-    constexpr int TM = 32 * MB;
+    using GEO = TileGeo<NB, BR>;
+    constexpr int TN = GEO::TN;
+    constexpr int TM = BR * MB;
     constexpr int RS = TN * 2 + 16; // LDS bytes per staged row
-    static_assert(TM * RS + 4 * TM <= TileGeo<NB>::lds_bytes(MB), "staging fits the tile's LDS");
-    const uint32_t *tbl = stage_row_index<DT, MB>(yr, rows, smem + TM * RS);
+    static_assert(TM * RS + 4 * TM <= GEO::lds_bytes(MB), "staging fits the tile's LDS");
+    const uint32_t *tbl = stage_row_index<TM>(yr, rows, smem + TM * RS);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        const int m = 32 * mb + tl.nl;
+        const int m = BR * mb + tl.nl;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int c = 32 * NB * tl.wave + 32 * nb + 8 * g4 + 4 * tl.h;
-                const float16_t &v = acc[nb][mb];
+            for (int g4 = 0; g4 < GEO::ACC / 4; ++g4) {
+                const int c = BR * NB * tl.wave + BR * nb + 4 * GEO::G * g4 + 4 * tl.g;
+                const auto &v = acc[nb][mb];
                 uint2 o;
                 o.x = f32x2_to_act2<DT>(v[4 * g4 + 0], v[4 * g4 + 1]);
                 o.y = f32x2_to_act2<DT>(v[4 * g4 + 2], v[4 * g4 + 3]);
@@ -433,27 +551,28 @@ __device__ __forceinline__ void tile_store(const float16_t (&acc)[NB][MB], const
 
 // Store with the fused stage-1 activation (paired layout, see FmtFP4): the
 // same accumulator register of blocks nb = 2 p and 2 p + 1 holds gate and up
-// of one output column, n = n0 + 16 NB w + 32 p + 8 g4 + 4 h + j, so
+// of one output column, n = n0 + (BR NB / 2) w + BR p + 4 G g4 + 4 g + j, so
 // out = silu(gate) * up in fp32 with silu(v) = v / (1 + e^-v), rounded once
 // to the activation dtype.  Staged through LDS as for tile_store: TN / 2
 // output columns per tile row.
-template <int DT, int NB, int MB, class YRows>
-__device__ __forceinline__ void tile_store_silu_mul(const float16_t (&acc)[NB][MB],
+template <int DT, int NB, int MB, int BR, class YRows>
+__device__ __forceinline__ void tile_store_silu_mul(const typename AccT<BR>::type (&acc)[NB][MB],
                                                    const YRows &yr, int rows, int n0, int I,
-                                                   const TileLane &tl, uint8_t *smem)
+                                                   const TileLane<BR> &tl, uint8_t *smem)
 {
-    constexpr int TN = TileGeo<NB>::TN;
-    constexpr int TM = 32 * MB;
+    using GEO = TileGeo<NB, BR>;
+    constexpr int TN = GEO::TN;
+    constexpr int TM = BR * MB;
     constexpr int RS = TN + 16; // LDS bytes per staged row (TN / 2 values + pad)
-    const uint32_t *tbl = stage_row_index<DT, MB>(yr, rows, smem + TM * RS);
+    const uint32_t *tbl = stage_row_index<TM>(yr, rows, smem + TM * RS);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        const int m = 32 * mb + tl.nl;
+        const int m = BR * mb + tl.nl;
 #pragma unroll
         for (int p = 0; p < NB / 2; ++p)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int c = 16 * NB * tl.wave + 32 * p + 8 * g4 + 4 * tl.h;
+            for (int g4 = 0; g4 < GEO::ACC / 4; ++g4) {
+                const int c = (BR * NB / 2) * tl.wave + BR * p + 4 * GEO::G * g4 + 4 * tl.g;
                 float o4[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -511,34 +630,39 @@ __device__ __forceinline__ int xcd_tile(int tiles, int nxcd)
 
 // W4A16: packed codes qweight[N][K/8], scales[N][K/g] in DT, packed
 // zero-points qzeros[N/8][K/g] (or none: z = 8).  Each lane handles rows
-// n_nb = n0 + 32 NB wave + 32 nb + nl, which share n % 8, so one nibble shift
-// of the zero-point words serves all its blocks.
-template <int DT, bool HAS_Z, int NB, bool GW>
+// n_nb = n0 + BR NB wave + BR nb + nl, which share n % 8, so one nibble shift
+// of the zero-point words serves all its blocks.  A lane's k of a span are
+// PPL 32-wide slices hf (k = 32 (PPL g + hf) ..), each inside one group.
+template <int DT, bool HAS_Z, int NB, bool GW, int BR = 32>
 struct FmtW4 {
+    static constexpr int PPL = TileGeo<NB, BR>::PPL;
     // GW: every group spans at least 64 k (g >= 64), so a lane's two 32-wide
-    // slices of a span share one scale and one zero-point word: one load each.
-    static constexpr int NLOADS = NB * (HAS_Z ? 2 : 1) * (GW ? 1 : 2);
+    // slices of a span (BR = 32) share one scale and one zero-point word: one
+    // load each.
+    static constexpr int LPS = GW ? 1 : PPL; // loads per block per span
+    static constexpr int NLOADS = NB * (HAS_Z ? 2 : 1) * LPS;
+    static constexpr bool ZERO_CODES = false; // slices past K: zero scales
     struct Meta {
-        uint32_t s[NB][2], z[NB][2];
+        uint32_t s[NB][PPL], z[NB][PPL];
     };
     const uint8_t *wq, *ws, *wz;
     uint32_t soff[NB], zoff[NB];
-    int K, gshift, h, zsh;
+    int K, gshift, g, zsh;
 
     __device__ FmtW4(const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
-                     int N, int K_, int gshift_, int n0, const TileLane &tl)
+                     int N, int K_, int gshift_, int n0, const TileLane<BR> &tl)
     {
         wq = reinterpret_cast<const uint8_t *>(qweight);
         ws = reinterpret_cast<const uint8_t *>(scales);
         wz = reinterpret_cast<const uint8_t *>(qzeros);
         K = K_;
         gshift = gshift_;
-        h = tl.h;
+        g = tl.g;
         zsh = 4 * (tl.nl & 7);
         const int G = K >> (5 + gshift);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int n = min(n0 + 32 * NB * tl.wave + 32 * nb + tl.nl, N - 1);
+            const int n = min(n0 + BR * NB * tl.wave + BR * nb + tl.nl, N - 1);
             soff[nb] = (uint32_t)n * (uint32_t)G * 2u;
             zoff[nb] = (uint32_t)(n >> 3) * (uint32_t)G * 4u;
         }
@@ -549,8 +673,8 @@ struct FmtW4 {
     __device__ __forceinline__ void load_meta(int span, Meta &m) const
     {
 #pragma unroll
-        for (int hf = 0; hf < (GW ? 1 : 2); ++hf) {
-            const int k = span * TL_SPAN + 64 * h + 32 * hf;
+        for (int hf = 0; hf < LPS; ++hf) {
+            const int k = span * TL_SPAN + 32 * (PPL * g + hf);
             const int kc = min(k, K - 32); // slice past K: clamped load, scale zeroed at use
             const uint32_t grp = (uint32_t)(kc >> (5 + gshift));
 #pragma unroll
@@ -560,21 +684,21 @@ struct FmtW4 {
                                     : 0x88888888u;
             }
         }
-        if constexpr (GW) {
+#pragma unroll
+        for (int hf = LPS; hf < PPL; ++hf)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                m.s[nb][1] = m.s[nb][0]; // separate copies: the tail zeroes them per slice
-                m.z[nb][1] = m.z[nb][0];
+                m.s[nb][hf] = m.s[nb][0]; // separate copies: the tail zeroes them per slice
+                m.z[nb][hf] = m.z[nb][0];
             }
-        }
     }
 
     // Slices past K: zero scales ((q - z) * 0 is a zero of either sign).
-    __device__ __forceinline__ void zero_past_k(int span, u32x4 (&)[NB][2], Meta &m) const
+    __device__ __forceinline__ void zero_past_k(int span, u32x4 (&)[NB][PPL], Meta &m) const
     {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-            if (span * TL_SPAN + 64 * h + 32 * hf >= K)
+        for (int hf = 0; hf < PPL; ++hf)
+            if (span * TL_SPAN + 32 * (PPL * g + hf) >= K)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
                     m.s[nb][hf] = 0u;
@@ -589,72 +713,81 @@ struct FmtW4 {
 };
 
 // MXFP4: E2M1 codes w_fp4[N][K/2] (even k in the low nibble), E8M0 scales
-// w_scale[N][K/32]; needs K % 64 == 0 so a lane's two 32-wide slices share
-// one aligned 16-bit scale load.
+// w_scale[N][K/32]; needs K % 64 == 0, so that with BR = 32 a lane's two
+// 32-wide slices share one aligned 16-bit scale load (BR = 16: one slice,
+// one byte).
 //
 // Paired layout (PAIRED, for the fused gate/up activation): the tile's
 // weight rows come in pairs, gate row j and up row N/2 + j, so that block
-// nb = 2 p of wave w holds gate rows n0 + 16 NB w + 32 p .. +31 and block
-// 2 p + 1 the matching up rows; tile row t = 32 NB w + 32 nb + i maps to
-// matrix row (nb % 2) * N/2 + n0 + 16 NB w + 32 (nb / 2) + i.
-template <bool PAIRED, int NB>
+// nb = 2 p of wave w holds gate rows n0 + (BR NB / 2) w + BR p .. +BR-1 and
+// block 2 p + 1 the matching up rows; tile row t = BR NB w + BR nb + i maps
+// to matrix row (nb % 2) * N/2 + n0 + (BR NB / 2) w + BR (nb / 2) + i.
+template <bool PAIRED, int NB, int BR = 32>
 struct FmtFP4 {
     static_assert(!PAIRED || NB % 2 == 0, "gate / up blocks come in pairs");
+    static constexpr int PPL = TileGeo<NB, BR>::PPL;
     static constexpr int NLOADS = NB;
+    static constexpr bool ZERO_CODES = true; // slices past K: zero codes
     struct Meta {
-        uint32_t s[NB]; // E8M0 bytes of slices hf = 0 (low byte) and 1
+        uint32_t s[NB]; // E8M0 bytes of slices hf = 0 (low byte) and 1 (BR = 32)
     };
     const uint8_t *wq, *ws;
     uint32_t soff[NB];
-    int K, h;
+    int K, g;
 
     __device__ FmtFP4(const uint8_t *w_fp4, const uint8_t *w_scale, int N, int K_, int n0,
-                      const TileLane &tl)
+                      const TileLane<BR> &tl)
     {
         wq = w_fp4;
         ws = w_scale;
         K = K_;
-        h = tl.h;
+        g = tl.g;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int n = tile_row(n0, N, 32 * NB * tl.wave + 32 * nb + tl.nl);
+            const int n = tile_row(n0, N, BR * NB * tl.wave + BR * nb + tl.nl);
             soff[nb] = (uint32_t)n * (uint32_t)(K >> 5);
         }
     }
 
-    // Matrix row of tile row t; PAIRED: t = 32 NB w + 32 nb + i is row
-    // (nb % 2) * N/2 + n0 + 16 NB w + 32 (nb / 2) + i (gate rows, then the
-    // matching up rows).
+    // Matrix row of tile row t; PAIRED: t = BR NB w + BR nb + i is row
+    // (nb % 2) * N/2 + n0 + (BR NB / 2) w + BR (nb / 2) + i (gate rows, then
+    // the matching up rows).
     __device__ __forceinline__ int tile_row(int n0, int N, int t) const
     {
         if constexpr (!PAIRED) {
             return min(n0 + t, N - 1);
         } else {
             const int half = N >> 1;
-            const int w = t / (32 * NB), nb = (t >> 5) % NB;
-            return (nb & 1) * half + min(n0 + 16 * NB * w + 32 * (nb >> 1) + (t & 31), half - 1);
+            const int w = t / (BR * NB), nb = (t / BR) % NB;
+            return (nb & 1) * half +
+                   min(n0 + (BR * NB / 2) * w + BR * (nb >> 1) + (t & (BR - 1)), half - 1);
         }
     }
 
     __device__ __forceinline__ void load_meta(int span, Meta &m) const
     {
-        const int k = min(span * TL_SPAN + 64 * h, K - 64); // past K: clamped, zeroed later
-        const uint32_t kg = (uint32_t)k >> 5;               // even
+        // past K: clamped, zeroed later
+        const int k = min(span * TL_SPAN + 32 * PPL * g, K - 32 * PPL);
+        const uint32_t kg = (uint32_t)k >> 5; // even when PPL = 2
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            m.s[nb] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + kg);
+        for (int nb = 0; nb < NB; ++nb) {
+            if constexpr (PPL == 2)
+                m.s[nb] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + kg);
+            else
+                m.s[nb] = ws[soff[nb] + kg];
+        }
     }
 
-    // Slices past K: zero codes (E2M1 code 0 is +0).  K % 64 == 0, so both
-    // 32-wide slices of a lane are inside K or both past it.
-    __device__ __forceinline__ void zero_past_k(int span, u32x4 (&cw)[NB][2], Meta &) const
+    // Slices past K: zero codes (E2M1 code 0 is +0).  K % 64 == 0, so with
+    // BR = 32 both 32-wide slices of a lane are inside K or both past it.
+    __device__ __forceinline__ void zero_past_k(int span, u32x4 (&cw)[NB][PPL], Meta &) const
     {
-        if (span * TL_SPAN + 64 * h >= K)
+        if (span * TL_SPAN + 32 * PPL * g >= K)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                cw[nb][0] = u32x4{0u, 0u, 0u, 0u};
-                cw[nb][1] = u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int hf = 0; hf < PPL; ++hf)
+                    cw[nb][hf] = u32x4{0u, 0u, 0u, 0u};
     }
 
     __device__ __forceinline__ u32x4 dequant(uint32_t word, const Meta &m, int nb, int st) const
