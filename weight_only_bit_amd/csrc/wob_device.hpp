@@ -149,7 +149,13 @@ __device__ __forceinline__ uint16_t f32_to_act(float f)
 template <int DT>
 __device__ __forceinline__ uint32_t f32x2_to_act2(float a, float b)
 {
-    return (uint32_t)f32_to_act<DT>(a) | ((uint32_t)f32_to_act<DT>(b) << 16);
+    // one packed conversion (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32, nearest
+    // even, as f32_to_act) instead of two conversions, a shift and an or
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    if constexpr (DT == DT_F16)
+        return bitcast<uint32_t>(__builtin_convertvector(f2_t{a, b}, half2_t));
+    else
+        return bitcast<uint32_t>(__builtin_convertvector(f2_t{a, b}, bf162_t));
 }
 
 
@@ -185,21 +191,36 @@ __device__ __forceinline__ half2_t f16_neg_bias_pair(uint32_t z)
     return bitcast<half2_t>((0xE400u | z) | ((0xD400u | (z << 4)) << 16));
 }
 
-// bfloat16: values from byte lanes as fp32, (q - z) * s exact in fp32 (the
-// product fits in 24 bits, and a zero difference keeps the IEEE sign of
-// 0 * s), one rounding to bfloat16 per value.
-__device__ __forceinline__ u32x4 w4_word_bf16x8(uint32_t w, float s, float zf)
+// bfloat16: the exact (q - z) pairs as binary16 (as w4_word_f16x8), each
+// value scaled in fp32 by one v_fma_mix_f32 (binary16 operand, fp32 scale,
+// addend -0): exactly (q - z) * s, since the product fits in 24 bits and the
+// -0 addend keeps the IEEE sign of a zero product (0 * s, and s's Inf or
+// NaN, pass through as in a multiply); one packed rounding to bfloat16 per
+// pair.  `mz` must hold -0.0f in a way the compiler cannot see (a constant
+// -0 addend is folded into a plain multiply, which costs a separate
+// binary16-to-fp32 conversion per value).
+__device__ __forceinline__ u32x4 w4_word_bf16x8(uint32_t w, float s, half2_t negb, float mz)
 {
-    const uint32_t lo = w & 0x0F0F0F0Fu;        // values 0, 2, 4, 6
-    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu; // values 1, 3, 5, 7
+    const half2_t mul = half2_t{(_Float16)1.0f, (_Float16)0.0625f};
     u32x4 o;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const float qe = (float)((lo >> (8 * p)) & 0xFFu);
-        const float qo = (float)((hi >> (8 * p)) & 0xFFu);
-        o[p] = f32x2_to_act2<DT_BF16>((qe - zf) * s, (qo - zf) * s);
+        const uint32_t sel = 0x04000400u | (uint32_t)p | ((uint32_t)p << 16);
+        const uint32_t t = __builtin_amdgcn_perm(MAGIC4_F16, w, sel) & 0xFFF0FF0Fu;
+        const half2_t d = __builtin_elementwise_fma(bitcast<half2_t>(t), mul, negb);
+        o[p] = f32x2_to_act2<DT_BF16>(__builtin_fmaf((float)d[0], s, mz),
+                                      __builtin_fmaf((float)d[1], s, mz));
     }
     return o;
+}
+
+// -0.0f in a register, opaque to the optimizer (for w4_word_bf16x8).  Not
+// volatile: the compiler may share and hoist it.
+__device__ __forceinline__ float opaque_neg_zero()
+{
+    float mz;
+    asm("v_mov_b32 %0, 0x80000000" : "=v"(mz));
+    return mz;
 }
 
 // One weight word of the MFMA operand form from the scale bits and zero-point.
@@ -210,7 +231,8 @@ __device__ __forceinline__ u32x4 w4_word_act8(uint32_t w, uint32_t sbits, uint32
         const _Float16 sh = bitcast<_Float16>((uint16_t)sbits);
         return w4_word_f16x8(w, f16_neg_bias_pair(z), half2_t{sh, sh});
     } else {
-        return w4_word_bf16x8(w, act_to_f32<DT_BF16>((uint16_t)sbits), (float)z);
+        return w4_word_bf16x8(w, act_to_f32<DT_BF16>((uint16_t)sbits), f16_neg_bias_pair(z),
+                              opaque_neg_zero());
     }
 }
 
