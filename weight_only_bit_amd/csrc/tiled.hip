@@ -156,11 +156,16 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
 
     int e = 0, m0, rows, nt;
     if (!m_offsets) {
+        // Dense: tiles in N-major order (activation tiles fastest), so each
+        // XCD's run covers a few weight tiles for every activation tile: the
+        // weights cross each XCD's L2 once and the activations (the smaller
+        // operand at prefill shapes) several times, instead of every XCD
+        // streaming all the weights past one activation tile.
         const int t = xcd_tile(n_mt * n_nt, nxcd);
         if (t < 0)
             return;
-        const int mt = t / n_nt;
-        nt = t - mt * n_nt;
+        nt = t / n_mt;
+        const int mt = t - nt * n_mt;
         m0 = mt * TMX;
         rows = min(TMX, M - m0);
     } else if (!grouped_tile(m_offsets, num_groups, M, TMX, n_nt, nxcd, e, m0, rows, nt)) {

@@ -612,9 +612,9 @@ __device__ __forceinline__ void tile_store_zero(const YRows &yr, int rows, int n
 
 // XCD-aware tile order: workgroups are dealt to the device's `nxcd` XCDs
 // round-robin (workgroup b runs on XCD b % nxcd); each XCD takes a contiguous
-// run of the `tiles` tiles (N fastest), so its workgroups share activation
-// rows in that XCD's L2.  The grid holds nxcd * ceil(tiles / nxcd)
-// workgroups; returns -1 for those beyond the run.
+// run of the `tiles` tile indices, so the tiles that share an operand (as the
+// caller orders them) share it in that XCD's L2.  The grid holds
+// nxcd * ceil(tiles / nxcd) workgroups; returns -1 for those beyond the run.
 __device__ __forceinline__ int xcd_tile(int tiles, int nxcd)
 {
     const int per_xcd = (tiles + nxcd - 1) / nxcd;
