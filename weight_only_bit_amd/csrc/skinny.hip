@@ -40,10 +40,14 @@
 // exponent byte of 1024 and one packed add of -(1024 + z) per pair removes
 // the bias; bfloat16: byte-to-float conversions, an fp32 subtract and a pack),
 // which v_dot2_f32_f16 / v_dot2_f32_bf16 multiply with the activation pairs.
+// The odd codes stay in their high nibbles (16 q, no shift), so their pairs
+// hold 16 (q - z) and their products accumulate separately at 16 times their
+// value; one fma with 1/16 joins the two sums (powers of two scale every
+// rounding exactly, so the result is the same as with unshifted codes).
 // |q - z| <= 15 has four significant bits, so every product is exact in fp32;
 // each chunk's sum of products sum_k (q_k - z) x_k is scaled once by its s.
 // The sums round only at the size of their own terms: weights that dequantize
-// to zero give exact zeros whatever the activations.  About 1.9 vector
+// to zero give exact zeros whatever the activations.  About 1.8 vector
 // operations per weight at M = 1 (binary16).
 //
 // Measured alternatives (MI355X, one box, decode 1 x 43008 x 5376): folding
@@ -281,10 +285,10 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
                 sc[o] = act_to_f32<DT>(SG ? (uint16_t)sv[o] : sp[8 * G * o + SU * i]);
                 const uint32_t z = HAS_Z ? nib(zp[G * o + SU * i], r) : 8u;
                 if constexpr (DT == DT_F16) {
-                    const uint32_t nb2 = f16_neg_bias2(z);
+                    const uint32_t nb2 = f16_neg_bias2(z), nb2h = f16_neg_bias2_hi(z);
 #pragma unroll
                     for (int wi = 0; wi < 4; ++wi)
-                        pr[o][wi] = w4_diff_pairs_f16(wv[o][wi], nb2);
+                        pr[o][wi] = w4_diff_pairs_f16(wv[o][wi], nb2, nb2h);
                 } else {
                     const float zf = (float)z;
 #pragma unroll
@@ -316,7 +320,9 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
                             a1 = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(pr[o][wi][3]), bitcast<bf162_t>(x4[3]), a1, false);
                         }
                     }
-                    acc[o][m] = fmaf(sc[o], a0 + a1, acc[o][m]);
+                    // a1 holds the odd codes' products at 16 times their value
+                    // (exactly, so a1 / 16 is the plain sum): a0 + a1 / 16
+                    acc[o][m] = fmaf(sc[o], fmaf(a1, 0.0625f, a0), acc[o][m]);
                 }
             }
         };

@@ -25,6 +25,7 @@ namespace wob {
 namespace {
 
 constexpr int TILED_NB = 2; // 32-row weight blocks per wave: 256 x 256 tiles
+constexpr int TILE_BAND = 4; // activation tiles per band of the dense tile order
 
 // Contiguous activation rows m0 .. m0 + rows - 1 of x[.][K] and y[.][N].
 // Byte offset of row min(16 i + rl, rows - 1): rowb (16 i + rl) clamped to
@@ -156,16 +157,22 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
 
     int e = 0, m0, rows, nt;
     if (!m_offsets) {
-        // Dense: tiles in N-major order (activation tiles fastest), so each
-        // XCD's run covers a few weight tiles for every activation tile: the
-        // weights cross each XCD's L2 once and the activations (the smaller
-        // operand at prefill shapes) several times, instead of every XCD
-        // streaming all the weights past one activation tile.
+        // Dense: tiles in bands of TILE_BAND activation tiles; within a band
+        // the weight tiles advance every TILE_BAND tiles (activation tiles
+        // fastest).  An XCD's contiguous run of tile indices is then a 2-D
+        // block (at the prefill shape, 4 activation tiles x 16 weight tiles,
+        // 4 x 8 of them resident at once), so both operands are shared in
+        // its L2: 4 x 2.75 MB of activations and 8 x 0.69 MB of weights per
+        // round, where a run along one operand shares only that one.
         const int t = xcd_tile(n_mt * n_nt, nxcd);
         if (t < 0)
             return;
-        nt = t / n_mt;
-        const int mt = t - nt * n_mt;
+        const int band = t / (TILE_BAND * n_nt);
+        const int mt0 = band * TILE_BAND;
+        const int bw = min(TILE_BAND, n_mt - mt0); // the last band may be narrower
+        const int local = t - mt0 * n_nt;
+        nt = local / bw;
+        const int mt = mt0 + (local - nt * bw);
         m0 = mt * TMX;
         rows = min(TMX, M - m0);
     } else if (!grouped_tile(m_offsets, num_groups, M, TMX, n_nt, nxcd, e, m0, rows, nt)) {

@@ -69,22 +69,34 @@ __device__ __forceinline__ uint32_t f16_neg_bias2(uint32_t z)
     return h | (h << 16);
 }
 
-// The four (q - z) pairs of a word in word order, as binary16: after masking,
-// the even codes sit in the bytes of t0 and the odd ones in t1; v_perm_b32
-// interleaves two of those bytes with the exponent byte 0x64 (exact 1024 + q)
-// and one packed add of -(1024 + z) per pair removes the bias exactly.
-// Eleven vector operations per word.
-__device__ __forceinline__ u32x4 w4_diff_pairs_f16(uint32_t w, uint32_t negb2)
+// The same for the odd codes, which w4_diff_pairs_f16 keeps in place in the
+// high nibble (16 q): -(1024 + 16 z) twice, leaving 16 (q - z) exactly.
+__device__ __forceinline__ uint32_t f16_neg_bias2_hi(uint32_t z)
 {
-    const uint32_t t0 = w & 0x0F0F0F0Fu;        // codes 0, 2, 4, 6 in bytes 0..3
-    const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu; // codes 1, 3, 5, 7
+    const uint32_t h = 0xE400u | (z << 4);
+    return h | (h << 16);
+}
+
+// The four (q - z) pairs of a word in word order, as binary16: after masking,
+// the even codes q sit in the low nibbles of t0 and the odd ones, as 16 q, in
+// the high nibbles of t1 (no shift); v_perm_b32 interleaves two of those bytes
+// with the exponent byte 0x64 (exact 1024 + q or 1024 + 16 q) and one packed
+// add per pair removes the bias exactly.  Pairs 0 and 2 hold (q - z), pairs
+// 1 and 3 hold 16 (q - z) (|16 (q - z)| <= 240, exact): callers scale the
+// products of the odd pairs by 1/16 once, which is exact.  Ten vector
+// operations per word.
+__device__ __forceinline__ u32x4 w4_diff_pairs_f16(uint32_t w, uint32_t negb2, uint32_t negb2_hi)
+{
+    const uint32_t t0 = w & 0x0F0F0F0Fu; // codes 0, 2, 4, 6 in bytes 0..3
+    const uint32_t t1 = w & 0xF0F0F0F0u; // 16 x codes 1, 3, 5, 7
     const half2_t nb = bitcast<half2_t>(negb2);
+    const half2_t nbh = bitcast<half2_t>(negb2_hi);
     u32x4 o;
     // selector bytes 0-3 pick from t (src1), 4 picks the magic byte (src0)
-    o[0] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t0, 0x04020400u)) + nb); // (v0, v4)
-    o[1] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t1, 0x04020400u)) + nb); // (v1, v5)
-    o[2] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t0, 0x04030401u)) + nb); // (v2, v6)
-    o[3] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t1, 0x04030401u)) + nb); // (v3, v7)
+    o[0] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t0, 0x04020400u)) + nb);  // (v0, v4)
+    o[1] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t1, 0x04020400u)) + nbh); // 16 (v1, v5)
+    o[2] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t0, 0x04030401u)) + nb);  // (v2, v6)
+    o[3] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t1, 0x04030401u)) + nbh); // 16 (v3, v7)
     return o;
 }
 
@@ -96,19 +108,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
     return bitcast<uint32_t>(__builtin_convertvector(f2_t{a, b}, bf162_t));
 }
 
-// The four (q - z) pairs of a word in word order, as bfloat16: each code byte
-// becomes an fp32 integer, z is subtracted exactly, and each pair is packed
-// to bfloat16 (|q - z| <= 15 is exact there).  gfx950 has no packed bfloat16
-// add, so this goes through fp32.
+// The four (q - z) pairs of a word in word order, as bfloat16, with the same
+// layout as w4_diff_pairs_f16 (pairs 1 and 3 hold 16 (q - z)): each code byte
+// becomes an fp32 integer, z (or 16 z) is subtracted exactly, and each pair is
+// packed to bfloat16 (|16 (q - z)| <= 240 is exact there).  gfx950 has no
+// packed bfloat16 add, so this goes through fp32.
 __device__ __forceinline__ u32x4 w4_diff_pairs_bf16(uint32_t w, float zf)
 {
-    const uint32_t t0 = w & 0x0F0F0F0Fu;        // codes 0, 2, 4, 6 in bytes 0..3
-    const uint32_t t1 = (w >> 4) & 0x0F0F0F0Fu; // codes 1, 3, 5, 7
+    const uint32_t t0 = w & 0x0F0F0F0Fu; // codes 0, 2, 4, 6 in bytes 0..3
+    const uint32_t t1 = w & 0xF0F0F0F0u; // 16 x codes 1, 3, 5, 7
+    const float zh = 16.0f * zf;
     u32x4 o;
     o[0] = pack_bf16x2((float)(t0 & 0xFFu) - zf, (float)((t0 >> 16) & 0xFFu) - zf); // (v0, v4)
-    o[1] = pack_bf16x2((float)(t1 & 0xFFu) - zf, (float)((t1 >> 16) & 0xFFu) - zf); // (v1, v5)
+    o[1] = pack_bf16x2((float)(t1 & 0xFFu) - zh, (float)((t1 >> 16) & 0xFFu) - zh); // 16 (v1, v5)
     o[2] = pack_bf16x2((float)((t0 >> 8) & 0xFFu) - zf, (float)(t0 >> 24) - zf);    // (v2, v6)
-    o[3] = pack_bf16x2((float)((t1 >> 8) & 0xFFu) - zf, (float)(t1 >> 24) - zf);    // (v3, v7)
+    o[3] = pack_bf16x2((float)((t1 >> 8) & 0xFFu) - zh, (float)(t1 >> 24) - zh);    // 16 (v3, v7)
     return o;
 }
 
