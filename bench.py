@@ -542,9 +542,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the weight-only GEMM path is single-GPU; see the sharding notes in DESIGN.md)",
-              file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported (each "
+              "GEMM call runs on one GPU: a sharded layer would run it on each GPU's N- or "
+              "K-slice of the weights)", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.reps < 1 or args.warmup < 0:
         print("bench.py: --steps and --reps must be >= 1, --warmup >= 0", file=sys.stderr)
