@@ -68,6 +68,7 @@ MALL_BYTES = 256 << 20         # Infinity Cache
 REUSE_BYTES = 2 * MALL_BYTES   # bytes touched between two uses of one operand copy
 MAX_COPIES = 512               # tiny calls: the cache cannot be defeated; labelled hot
 SETTLE_S = 0.3                 # untimed replays before each timed series (clock ramp)
+COVER_CYCLES = 400_000         # spin ahead of each timed replay (~0.2 ms) to cover its submission
 _settle_s = SETTLE_S           # --settle-s
 FETCH_FACTOR_DEFAULT = 2.0     # FETCH_SIZE reads half of a device copy's bytes on this part
 TRAFFIC_SOURCE = ("committed rocprofv3 counters (profiles/traffic.json: FETCH_SIZE x fetch "
@@ -201,6 +202,11 @@ def time_steps(step, steps: int, warmup: int, copies: int, reps: int) -> Timing:
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        # A spin kernel ahead of the start event keeps the GPU busy while the
+        # host submits the graph, so the timed span holds the K calls back to
+        # back and not the submission latency (which a model's graph of many
+        # layers amortizes over all of them, not over K calls).
+        torch.cuda._sleep(COVER_CYCLES)
         start.record(stream)
         graphs[r % ngraphs].replay()
         end.record(stream)
