@@ -36,7 +36,7 @@
 // runs in one generation (21.1 -> 16.8 us measured).
 //
 // Arithmetic: each word becomes four pairs of exact (q - z) values in the
-// activation dtype (binary16: byte permutes place each code under the
+// activation dtype (binary16: one and-or per pair places two codes under the
 // exponent byte of 1024 and one packed add of -(1024 + z) per pair removes
 // the bias; bfloat16: byte-to-float conversions, an fp32 subtract and a pack),
 // which v_dot2_f32_f16 / v_dot2_f32_bf16 multiply with the activation pairs.
@@ -47,8 +47,9 @@
 // |q - z| <= 15 has four significant bits, so every product is exact in fp32;
 // each chunk's sum of products sum_k (q_k - z) x_k is scaled once by its s.
 // The sums round only at the size of their own terms: weights that dequantize
-// to zero give exact zeros whatever the activations.  About 1.8 vector
-// operations per weight at M = 1 (binary16).
+// to zero give exact zeros whatever the activations.  About 1.9 vector
+// operations per weight at M = 1 (binary16), counting the scale, zero-point
+// and address work.
 //
 // Measured alternatives (MI355X, one box, decode 1 x 43008 x 5376): folding
 // the zero-point out of the sums as sum (B + q) x - (B + z) sum x with the

@@ -77,26 +77,38 @@ __device__ __forceinline__ uint32_t f16_neg_bias2_hi(uint32_t z)
     return h | (h << 16);
 }
 
-// The four (q - z) pairs of a word in word order, as binary16: after masking,
-// the even codes q sit in the low nibbles of t0 and the odd ones, as 16 q, in
-// the high nibbles of t1 (no shift); v_perm_b32 interleaves two of those bytes
-// with the exponent byte 0x64 (exact 1024 + q or 1024 + 16 q) and one packed
-// add per pair removes the bias exactly.  Pairs 0 and 2 hold (q - z), pairs
-// 1 and 3 hold 16 (q - z) (|16 (q - z)| <= 240, exact): callers scale the
-// products of the odd pairs by 1/16 once, which is exact.  Ten vector
-// operations per word.
+// The four (q - z) pairs of a word in word order, as binary16.  Codes 0 and 4
+// sit in the low nibbles of the word's two halves, codes 1 and 5 in the
+// nibbles above them, and a shift by 8 brings codes 2, 6 and 3, 7 to the same
+// places.  One and-or per pair keeps a pair's two nibbles and sets the
+// exponent byte 0x64 above them: 1024 + q, or 1024 + 16 q for the odd codes,
+// which stay in the high nibble (no shift).  One packed add per pair removes
+// the bias exactly.  Pairs 0 and 2 hold (q - z), pairs 1 and 3 hold 16 (q - z)
+// (|16 (q - z)| <= 240, exact): callers scale the products of the odd pairs by
+// 1/16 once, which is exact.  Nine vector operations per word (one shift,
+// four and-or, four packed adds); byte permutes of the masked word took ten.
+// 0x64006400 in a register, opaque to the optimizer: with both constants of
+// (a & m) | c known, the compiler emits a separate and and or (gfx950's
+// three-operand encoding takes no literal); with c in a register it forms one
+// v_and_or_b32.  Not volatile: the compiler may share and hoist it.
+__device__ __forceinline__ uint32_t opaque_f16_magic2()
+{
+    uint32_t r;
+    asm("v_mov_b32 %0, 0x64006400" : "=v"(r));
+    return r;
+}
+
 __device__ __forceinline__ u32x4 w4_diff_pairs_f16(uint32_t w, uint32_t negb2, uint32_t negb2_hi)
 {
-    const uint32_t t0 = w & 0x0F0F0F0Fu; // codes 0, 2, 4, 6 in bytes 0..3
-    const uint32_t t1 = w & 0xF0F0F0F0u; // 16 x codes 1, 3, 5, 7
     const half2_t nb = bitcast<half2_t>(negb2);
     const half2_t nbh = bitcast<half2_t>(negb2_hi);
     u32x4 o;
-    // selector bytes 0-3 pick from t (src1), 4 picks the magic byte (src0)
-    o[0] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t0, 0x04020400u)) + nb);  // (v0, v4)
-    o[1] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t1, 0x04020400u)) + nbh); // 16 (v1, v5)
-    o[2] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t0, 0x04030401u)) + nb);  // (v2, v6)
-    o[3] = bitcast<uint32_t>(bitcast<half2_t>(__builtin_amdgcn_perm(MAGIC4_F16, t1, 0x04030401u)) + nbh); // 16 (v3, v7)
+    const uint32_t w8 = w >> 8;
+    const uint32_t mg = opaque_f16_magic2();
+    o[0] = bitcast<uint32_t>(bitcast<half2_t>((w & 0x000F000Fu) | mg) + nb);   // (v0, v4)
+    o[1] = bitcast<uint32_t>(bitcast<half2_t>((w & 0x00F000F0u) | mg) + nbh);  // 16 (v1, v5)
+    o[2] = bitcast<uint32_t>(bitcast<half2_t>((w8 & 0x000F000Fu) | mg) + nb);  // (v2, v6)
+    o[3] = bitcast<uint32_t>(bitcast<half2_t>((w8 & 0x00F000F0u) | mg) + nbh); // 16 (v3, v7)
     return o;
 }
 
