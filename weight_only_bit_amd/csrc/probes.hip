@@ -34,11 +34,9 @@ __global__ __launch_bounds__(256) void w4a16_dequant_kernel(
     const uint16_t sbits = scales[(size_t)n * G + j];
     float vals[8];
     if constexpr (OUT_F32) {
-        // the skinny kernel's exact (q - z) pairs (word order, its helpers;
-        // pairs 1 and 3 come 16 times larger and are scaled by 1/16 as that
-        // kernel does), times the scale in fp32 here: that kernel applies the
-        // scale to each chunk's sum of products instead, and (q - z) * s is
-        // exact either way
+        // the skinny kernel's exact (q - z) pairs (word order, its helpers),
+        // times the scale in fp32 here: that kernel applies the scale to each
+        // chunk's sum of products instead, and (q - z) * s is exact either way
         const float s = act_to_f32<DT>(sbits);
         u32x4 d;
         if constexpr (DT == DT_F16)
@@ -56,9 +54,8 @@ __global__ __launch_bounds__(256) void w4a16_dequant_kernel(
                 lo = bitcast<float>(d[p] << 16);
                 hi = bitcast<float>(d[p] & 0xFFFF0000u);
             }
-            const float f = (p & 1) ? 0.0625f : 1.0f;
-            vals[word_order_value(2 * p)] = lo * f * s;
-            vals[word_order_value(2 * p + 1)] = hi * f * s;
+            vals[word_order_value(2 * p)] = lo * s;
+            vals[word_order_value(2 * p + 1)] = hi * s;
         }
         float *o = static_cast<float *>(out) + (size_t)idx * 8;
 #pragma unroll

@@ -40,10 +40,9 @@
 // exponent byte of 1024 and one packed add of -(1024 + z) per pair removes
 // the bias; bfloat16: byte-to-float conversions, an fp32 subtract and a pack),
 // which v_dot2_f32_f16 / v_dot2_f32_bf16 multiply with the activation pairs.
-// The odd codes stay in their high nibbles (16 q, no shift), so their pairs
-// hold 16 (q - z) and their products accumulate separately at 16 times their
-// value; one fma with 1/16 joins the two sums (powers of two scale every
-// rounding exactly, so the result is the same as with unshifted codes).
+// The odd codes stay in their high nibbles (16 q, no shift) and are read at
+// their plain value (under the binary16 exponent of 64, or by an exact fma
+// with 1/16 in fp32).
 // |q - z| <= 15 has four significant bits, so every product is exact in fp32;
 // each chunk's sum of products sum_k (q_k - z) x_k is scaled once by its s.
 // The sums round only at the size of their own terms: weights that dequantize
@@ -305,25 +304,19 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
                     xv[wi] = xb0[m * RB + 32 * i + 8 * wi];
 #pragma unroll
                 for (int o = 0; o < RO; ++o) {
-                    float a0 = 0.f, a1 = 0.f;
+                    float a = 0.f;
 #pragma unroll
                     for (int wi = 0; wi < 4; ++wi) {
                         const u32x4 x4 = xv[wi];
-                        if constexpr (DT == DT_F16) {
-                            a0 = __builtin_amdgcn_fdot2(bitcast<half2_t>(pr[o][wi][0]), bitcast<half2_t>(x4[0]), a0, false);
-                            a1 = __builtin_amdgcn_fdot2(bitcast<half2_t>(pr[o][wi][1]), bitcast<half2_t>(x4[1]), a1, false);
-                            a0 = __builtin_amdgcn_fdot2(bitcast<half2_t>(pr[o][wi][2]), bitcast<half2_t>(x4[2]), a0, false);
-                            a1 = __builtin_amdgcn_fdot2(bitcast<half2_t>(pr[o][wi][3]), bitcast<half2_t>(x4[3]), a1, false);
-                        } else {
-                            a0 = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(pr[o][wi][0]), bitcast<bf162_t>(x4[0]), a0, false);
-                            a1 = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(pr[o][wi][1]), bitcast<bf162_t>(x4[1]), a1, false);
-                            a0 = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(pr[o][wi][2]), bitcast<bf162_t>(x4[2]), a0, false);
-                            a1 = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(pr[o][wi][3]), bitcast<bf162_t>(x4[3]), a1, false);
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) {
+                            if constexpr (DT == DT_F16)
+                                a = __builtin_amdgcn_fdot2(bitcast<half2_t>(pr[o][wi][p]), bitcast<half2_t>(x4[p]), a, false);
+                            else
+                                a = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf162_t>(pr[o][wi][p]), bitcast<bf162_t>(x4[p]), a, false);
                         }
                     }
-                    // a1 holds the odd codes' products at 16 times their value
-                    // (exactly, so a1 / 16 is the plain sum): a0 + a1 / 16
-                    acc[o][m] = fmaf(sc[o], fmaf(a1, 0.0625f, a0), acc[o][m]);
+                    acc[o][m] = fmaf(sc[o], a, acc[o][m]);
                 }
             }
         };
@@ -331,14 +324,33 @@ __global__ __launch_bounds__(SK_MAX_THREADS, (sk_min_waves<M, RO>())) void w4a16
         // with chunk i + d + D.  Loads here are unconditional so the wait
         // counts stay exact; the scheduling barriers keep the compiler from
         // moving a refill across the computation it should overlap.
+        // The refill addresses advance by one pointer step per iteration, so
+        // the D loads of an iteration differ by immediate offsets.
         int i = 0;
+        const u32x4 *wq[RO];
+        const uint16_t *sq[RO];
+#pragma unroll
+        for (int o = 0; o < RO; ++o) {
+            wq[o] = wp[o] + 8 * D; // chunk i + D of this lane at i = 0
+            sq[o] = sg[o] + SU * D;
+        }
         for (; i + 2 * D <= n_it; i += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 chunk(i + d, ring[d], sring[d]);
                 __builtin_amdgcn_sched_barrier(0);
-                load_chunk(ring[d], sring[d], i + d + D);
+#pragma unroll
+                for (int o = 0; o < RO; ++o) {
+                    ring[d][o] = __builtin_nontemporal_load(wq[o] + 8 * d); // chunk i + d + D
+                    if constexpr (SG)
+                        sring[d][o] = sq[o][SU * d];
+                }
                 __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int o = 0; o < RO; ++o) {
+                wq[o] += 8 * D;
+                sq[o] += SU * D;
             }
         }
         // Drain: the ring holds chunks i .. i+D-1 (those below n_it) and fewer

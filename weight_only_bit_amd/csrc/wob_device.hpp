@@ -69,46 +69,47 @@ __device__ __forceinline__ uint32_t f16_neg_bias2(uint32_t z)
     return h | (h << 16);
 }
 
-// The same for the odd codes, which w4_diff_pairs_f16 keeps in place in the
-// high nibble (16 q): -(1024 + 16 z) twice, leaving 16 (q - z) exactly.
+// The same for the odd codes, which w4_diff_pairs_f16 reads in place in the
+// high nibble under the exponent of 64: -(64 + z) twice.
 __device__ __forceinline__ uint32_t f16_neg_bias2_hi(uint32_t z)
 {
-    const uint32_t h = 0xE400u | (z << 4);
+    const uint32_t h = 0xD400u | (z << 4);
     return h | (h << 16);
+}
+
+// Two binary16 exponent patterns in registers, opaque to the optimizer: with
+// both constants of (a & m) | c known, the compiler emits a separate and and
+// or (gfx950's three-operand encoding takes no literal); with c in a register
+// it forms one v_and_or_b32.  Not volatile: the compiler may share and hoist
+// them.
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t v)
+{
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+    return r;
 }
 
 // The four (q - z) pairs of a word in word order, as binary16.  Codes 0 and 4
 // sit in the low nibbles of the word's two halves, codes 1 and 5 in the
 // nibbles above them, and a shift by 8 brings codes 2, 6 and 3, 7 to the same
-// places.  One and-or per pair keeps a pair's two nibbles and sets the
-// exponent byte 0x64 above them: 1024 + q, or 1024 + 16 q for the odd codes,
-// which stay in the high nibble (no shift).  One packed add per pair removes
-// the bias exactly.  Pairs 0 and 2 hold (q - z), pairs 1 and 3 hold 16 (q - z)
-// (|16 (q - z)| <= 240, exact): callers scale the products of the odd pairs by
-// 1/16 once, which is exact.  Nine vector operations per word (one shift,
-// four and-or, four packed adds); byte permutes of the masked word took ten.
-// 0x64006400 in a register, opaque to the optimizer: with both constants of
-// (a & m) | c known, the compiler emits a separate and and or (gfx950's
-// three-operand encoding takes no literal); with c in a register it forms one
-// v_and_or_b32.  Not volatile: the compiler may share and hoist it.
-__device__ __forceinline__ uint32_t opaque_f16_magic2()
-{
-    uint32_t r;
-    asm("v_mov_b32 %0, 0x64006400" : "=v"(r));
-    return r;
-}
-
+// places.  One and-or per pair keeps a pair's two nibbles and sets an
+// exponent above them: 0x6400 over a low nibble reads as the exact binary16
+// 1024 + q, 0x5400 over a high nibble (16 q in the mantissa, whose unit there
+// is 1/16) as the exact 64 + q.  One packed add of -(1024 + z) or -(64 + z)
+// per pair removes the bias exactly.  Nine vector operations per word (one
+// shift, four and-or, four packed adds); byte permutes of the masked word
+// took ten.
 __device__ __forceinline__ u32x4 w4_diff_pairs_f16(uint32_t w, uint32_t negb2, uint32_t negb2_hi)
 {
     const half2_t nb = bitcast<half2_t>(negb2);
     const half2_t nbh = bitcast<half2_t>(negb2_hi);
-    u32x4 o;
     const uint32_t w8 = w >> 8;
-    const uint32_t mg = opaque_f16_magic2();
-    o[0] = bitcast<uint32_t>(bitcast<half2_t>((w & 0x000F000Fu) | mg) + nb);   // (v0, v4)
-    o[1] = bitcast<uint32_t>(bitcast<half2_t>((w & 0x00F000F0u) | mg) + nbh);  // 16 (v1, v5)
-    o[2] = bitcast<uint32_t>(bitcast<half2_t>((w8 & 0x000F000Fu) | mg) + nb);  // (v2, v6)
-    o[3] = bitcast<uint32_t>(bitcast<half2_t>((w8 & 0x00F000F0u) | mg) + nbh); // 16 (v3, v7)
+    const uint32_t e1024 = opaque_u32(0x64006400u), e64 = opaque_u32(0x54005400u);
+    u32x4 o;
+    o[0] = bitcast<uint32_t>(bitcast<half2_t>((w & 0x000F000Fu) | e1024) + nb);  // (v0, v4)
+    o[1] = bitcast<uint32_t>(bitcast<half2_t>((w & 0x00F000F0u) | e64) + nbh);   // (v1, v5)
+    o[2] = bitcast<uint32_t>(bitcast<half2_t>((w8 & 0x000F000Fu) | e1024) + nb); // (v2, v6)
+    o[3] = bitcast<uint32_t>(bitcast<half2_t>((w8 & 0x00F000F0u) | e64) + nbh);  // (v3, v7)
     return o;
 }
 
@@ -121,20 +122,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 }
 
 // The four (q - z) pairs of a word in word order, as bfloat16, with the same
-// layout as w4_diff_pairs_f16 (pairs 1 and 3 hold 16 (q - z)): each code byte
-// becomes an fp32 integer, z (or 16 z) is subtracted exactly, and each pair is
-// packed to bfloat16 (|16 (q - z)| <= 240 is exact there).  gfx950 has no
-// packed bfloat16 add, so this goes through fp32.
+// layout as w4_diff_pairs_f16: each code byte becomes an fp32 integer (the odd
+// codes in place as 16 q, brought back to q by an fma with 1/16), z is
+// subtracted exactly, and each pair is packed to bfloat16 (|q - z| <= 15 is
+// exact there).  gfx950 has no packed bfloat16 add, so this goes through fp32.
 __device__ __forceinline__ u32x4 w4_diff_pairs_bf16(uint32_t w, float zf)
 {
     const uint32_t t0 = w & 0x0F0F0F0Fu; // codes 0, 2, 4, 6 in bytes 0..3
     const uint32_t t1 = w & 0xF0F0F0F0u; // 16 x codes 1, 3, 5, 7
-    const float zh = 16.0f * zf;
+    const float nz = -zf;
+    auto hi = [&](uint32_t b) { return __builtin_fmaf((float)b, 0.0625f, nz); };
     u32x4 o;
     o[0] = pack_bf16x2((float)(t0 & 0xFFu) - zf, (float)((t0 >> 16) & 0xFFu) - zf); // (v0, v4)
-    o[1] = pack_bf16x2((float)(t1 & 0xFFu) - zh, (float)((t1 >> 16) & 0xFFu) - zh); // 16 (v1, v5)
+    o[1] = pack_bf16x2(hi(t1 & 0xFFu), hi((t1 >> 16) & 0xFFu));                    // (v1, v5)
     o[2] = pack_bf16x2((float)((t0 >> 8) & 0xFFu) - zf, (float)(t0 >> 24) - zf);    // (v2, v6)
-    o[3] = pack_bf16x2((float)((t1 >> 8) & 0xFFu) - zh, (float)(t1 >> 24) - zh);    // 16 (v3, v7)
+    o[3] = pack_bf16x2(hi((t1 >> 8) & 0xFFu), hi(t1 >> 24));                        // (v3, v7)
     return o;
 }
 
