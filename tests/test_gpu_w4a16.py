@@ -82,9 +82,10 @@ SPLIT_K = [(1, 1056, 32), (1, 2176, 128), (1, 4224, 64), (1, 5408, 32), (1, 6944
 @pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
 @pytest.mark.parametrize("M,K,g", SPLIT_K)
 def test_skinny_split_k_ring(wob, oracle, dtype, M, K, g):
-    # N = 2048 splits K over the waves of a workgroup: 2 to 17 chunks per lane,
-    # lanes of one wave one chunk apart in the last K slice, so the load ring's
-    # steady state, its drain and the clamped refills all run.
+    # N = 2048 splits K 2, 4 or 8 ways over the waves of a workgroup: 1 to 9
+    # chunks per lane, lanes of one wave one chunk apart in the last K slice,
+    # so the load ring's steady state, its drain and the clamped refills all
+    # run.
     d = wl.w4a16_inputs(M, 2048, K, g, dtype, seed=K + M, symmetric=(K % 3 == 0))
     _check(oracle, d, _run(wob, d, wob.PATH_SKINNY))
 

@@ -461,12 +461,15 @@ SkCfg sk_config(int M, int N, int K, int cus)
         }
         return best;
     }
-    // Few row octets: split K across the waves of a workgroup, keeping at
-    // least two chunks per lane.
+    // Few row octets: split K across the waves of a workgroup (up to 8 ways,
+    // one octet per workgroup beyond 4), keeping at least two chunks per
+    // lane.  On 1 x 5376 x 21504 the 8-way split (21 waves per CU instead of
+    // 10.5) ran 17.3 -> 15.9 us; splitting the 1 x 16384 x 5376 shape 3 or 4
+    // ways instead of 2 was slower (12.7 and 13.6 against 11.5 us).
     int ksplit = 1;
-    while (ksplit < SK_WAVES && octs * ksplit < 4096 && C >= 16 * ksplit * 2)
+    while (ksplit < SK_MAX_WAVES && octs * ksplit < 4096 && C >= 16 * ksplit * 2)
         ksplit *= 2;
-    return SkCfg{1, SK_WAVES, ksplit};
+    return SkCfg{1, max(SK_WAVES, ksplit), ksplit};
 }
 
 int lds_bytes(int M, int N, int K, int g)
