@@ -420,38 +420,53 @@ __global__ __launch_bounds__(CB_THREADS) void moe_combine_kernel(
 // tile's activation rows are gathered by token into LDS; each code word is
 // expanded with v_cvt_scalef32_pk_bf16_fp4 (the same conversion as the tile
 // kernel) and multiplied with v_dot2_f32_bf16 against the activation pairs
-// (exact products, fp32 accumulation).  A lane's chunks stream through a
-// ring of MG_D slots that is filled as soon as the expert is known: a
-// 2880-long row gives a lane at most 12 chunks, so its whole slice is in
-// flight at once, behind the listing and the activation staging, and the
-// workgroup waits for memory about twice (ids, then weights) instead of once
-// per batch.  With the fused activation a wave's rows are 4 gate rows and
-// the matching 4 up rows.
+// (exact products, fp32 accumulation).  As soon as the expert is known the
+// workgroup requests its rows' E8M0 scale bytes (a few coalesced 2-byte loads
+// per thread, stored in LDS after the listing) and then the first MG_D code
+// chunks of every lane; a lane's chunks stream through that ring of MG_D
+// slots.  Measured on 4 tokens x top-4 of 32 experts (K 2880, N 5760): a
+// scale byte loaded per chunk beside the codes cost about 15 % (a copy of
+// the kernel without scale loads ran 26.8 against 31.4 us); staging them in
+// LDS after the listing was slower (33.5), staging them ahead of the codes
+// faster (30.4); with staged scales a ring of 3 chunks beat 6 and 12 (33.6,
+// 33.4), and 8-wave workgroups matched 4-wave ones.  With the fused
+// activation a wave's rows are 4 gate rows and the matching 4 up rows.
 constexpr int MG_TOKENS = 8;  // decode path: T <= 8
 constexpr int MG_WAVES = 4;
 constexpr int MG_THREADS = 64 * MG_WAVES;
-constexpr int MG_D = 12;      // chunk slots per lane in the load ring
+constexpr int MG_D = 3;       // chunk slots per lane in the load ring
 constexpr int MG_LDS = 64 * 1024;
+constexpr int MG_BATCH = 4;   // staging loads per thread in flight
+// Scale units (2 bytes) per thread requested with the first code chunks:
+// all of them for K <= 3072 (MG_ROWS rows x K / 64 units).
+constexpr int MG_SB = 6;
 
 template <bool ACT>
 constexpr int mg_cols() { return ACT ? 4 * MG_WAVES : 8 * MG_WAVES; } // output columns per workgroup
 
+// Weight rows per workgroup (8 per wave) and the bytes of their staged E8M0
+// scales (K / 32 per row, padded to 16 bytes).
+constexpr int MG_ROWS = 8 * MG_WAVES;
+inline int mg_scale_bytes(int K) { return (MG_ROWS * (K >> 5) + 15) & ~15; }
+
 // Activation rows per pass for this K: the largest power of two <= 8 whose
-// rows fit the LDS budget (0: K too long for this path).
+// rows fit the LDS budget beside the staged scales (0: K too long for this
+// path).
 int mg_rows(int K)
 {
     int mr = 8;
-    while (mr > 0 && mr * 2 * K > MG_LDS)
+    while (mr > 0 && mr * 2 * K + mg_scale_bytes(K) > MG_LDS)
         mr >>= 1;
     return mr;
 }
 
-// A lane's code chunk i (chunk q + 8 i of its row, clamped into the row) and
-// its E8M0 scale byte.
+// A lane's code chunk i (chunk q + 8 i of its row, clamped into the row).
+// The chunk's E8M0 scale byte comes from the workgroup's staged scale rows.
 struct MgRow {
-    const uint8_t *w, *s; // the row's codes and scale bytes
-    int CK, q;            // chunks per row, this lane's first chunk
-    __device__ __forceinline__ void load(int i, u32x4 &wv, uint32_t &sb) const
+    const uint8_t *w; // the row's codes
+    const uint8_t *s; // the row's staged scale bytes (LDS)
+    int CK, q;        // chunks per row, this lane's first chunk
+    __device__ __forceinline__ void load(int i, u32x4 &wv) const
     {
         int j = min(q + 8 * i, CK - 1);
         // opaque to the optimizer: otherwise every ring slot keeps its own
@@ -459,7 +474,6 @@ struct MgRow {
         // slot), which costs more registers than the slots themselves
         asm volatile("" : "+v"(j));
         wv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w) + j);
-        sb = s[j];
     }
 };
 
@@ -493,8 +507,7 @@ __device__ __forceinline__ void mg_chunk(const u32x4 &w, uint32_t sb, const uint
 // One pass over the staged rows 0 .. mr-1 (MR >= mr): stream the lane's
 // chunks (the ring holds chunks 0 .. MG_D-1 on entry), reduce, store.
 template <bool ACT, int MR>
-__device__ __forceinline__ void mg_pass(const MgRow &wr, u32x4 (&rw)[MG_D],
-                                        uint32_t (&rs)[MG_D], const uint8_t *smem, int K2,
+__device__ __forceinline__ void mg_pass(const MgRow &wr, u32x4 (&rw)[MG_D], const uint8_t *smem, int K2,
                                         const int32_t *pairs, int mr, int col, bool cvalid,
                                         int lane, uint16_t *y, int Nout)
 {
@@ -509,9 +522,9 @@ __device__ __forceinline__ void mg_pass(const MgRow &wr, u32x4 (&rw)[MG_D],
     for (; i + 2 * MG_D <= nch; i += MG_D) {
 #pragma unroll
         for (int d = 0; d < MG_D; ++d) {
-            mg_chunk<MR>(rw[d], rs[d], smem, wr.q + 8 * (i + d), K2, mr, acc);
+            mg_chunk<MR>(rw[d], wr.s[wr.q + 8 * (i + d)], smem, wr.q + 8 * (i + d), K2, mr, acc);
             __builtin_amdgcn_sched_barrier(0);
-            wr.load(i + d + MG_D, rw[d], rs[d]);
+            wr.load(i + d + MG_D, rw[d]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -521,9 +534,9 @@ __device__ __forceinline__ void mg_pass(const MgRow &wr, u32x4 (&rw)[MG_D],
 #pragma unroll
         for (int d = 0; d < MG_D; ++d) {
             if (i + d < nch)
-                mg_chunk<MR>(rw[d], rs[d], smem, wr.q + 8 * (i + d), K2, mr, acc);
+                mg_chunk<MR>(rw[d], wr.s[wr.q + 8 * (i + d)], smem, wr.q + 8 * (i + d), K2, mr, acc);
             __builtin_amdgcn_sched_barrier(0);
-            wr.load(min(i + MG_D + d, max(nch - 1, 0)), rw[d], rs[d]);
+            wr.load(min(i + MG_D + d, max(nch - 1, 0)), rw[d]);
             __builtin_amdgcn_sched_barrier(0);
         }
         i += MG_D;
@@ -531,7 +544,7 @@ __device__ __forceinline__ void mg_pass(const MgRow &wr, u32x4 (&rw)[MG_D],
 #pragma unroll
     for (int d = 0; d < MG_D; ++d) {
         if (i + d < nch)
-            mg_chunk<MR>(rw[d], rs[d], smem, wr.q + 8 * (i + d), K2, mr, acc);
+            mg_chunk<MR>(rw[d], wr.s[wr.q + 8 * (i + d)], smem, wr.q + 8 * (i + d), K2, mr, acc);
         __builtin_amdgcn_sched_barrier(0); // one chunk's unpacked words live at a time
     }
     // Sum over the 8 lanes of a row; lane q = 0 holds row r's dot products.
@@ -586,35 +599,75 @@ __global__ __launch_bounds__(MG_THREADS) void moe_gemv_kernel(
     if (__syncthreads_or((j0 < p && b0 == e) || (j1 < p && b1 == e)))
         return; // an earlier workgroup slot owns this bucket
     const int Nout = ACT ? N / 2 : N;
-    // This lane's weight row and output column (rows past the matrix are
-    // clamped and never stored).
+    // Weight row and output column of the workgroup's row rho = 8 wave + r
+    // (rows past the matrix are clamped and never stored).
+    auto row_col = [&](int rho, int &col_, int &n_) {
+        const int w_ = rho >> 3, r_ = rho & 7;
+        if constexpr (ACT) {
+            col_ = slice * COLS + 4 * w_ + (r_ & 3);
+            n_ = (r_ >> 2) * (N / 2) + min(col_, N / 2 - 1);
+        } else {
+            col_ = slice * COLS + 8 * w_ + r_;
+            n_ = min(col_, N - 1);
+        }
+    };
     int col, n;
-    if constexpr (ACT) {
-        col = slice * COLS + 4 * wave + (r & 3);
-        n = (r >> 2) * (N / 2) + min(col, N / 2 - 1);
-    } else {
-        col = slice * COLS + 8 * wave + r;
-        n = min(col, N - 1);
-    }
+    row_col(8 * wave + r, col, n);
     const bool cvalid = col < Nout;
     const int CK = K >> 5;
     const int ee = min(e, E - 1); // the invalid bucket streams nothing (loads clamped, unused)
+    const int K2 = 2 * K;
+    uint8_t *const sl = smem + (size_t)MR * K2; // staged scale rows, CK bytes each
     MgRow wr;
     wr.w = w_fp4 + ((size_t)ee * N + n) * (size_t)(K >> 1);
-    wr.s = w_scale + ((size_t)ee * N + n) * (size_t)CK;
+    wr.s = sl + (size_t)(8 * wave + r) * CK;
     wr.CK = CK;
     wr.q = q;
     u32x4 rw[MG_D];
-    uint32_t rs[MG_D];
     auto fill = [&]() {
         // this lane's last chunk (a lane with no chunk, K < 256, loads chunk 0 unused)
         const int last = max(((CK - q + 7) >> 3) - 1, 0);
 #pragma unroll
         for (int d = 0; d < MG_D; ++d)
-            wr.load(min(d, last), rw[d], rs[d]);
+            wr.load(min(d, last), rw[d]);
     };
-    if (e < E)
+    // Cooperative copy of `tot` units, MG_BATCH loads per thread in flight
+    // before their stores (a plain loop waits one round trip per unit).
+    auto stage = [&](int tot, auto &&ld, auto &&st) __attribute__((always_inline)) {
+        for (int base = tid; base < tot; base += MG_BATCH * MG_THREADS) {
+            decltype(ld(0)) v[MG_BATCH];
+#pragma unroll
+            for (int b = 0; b < MG_BATCH; ++b)
+                v[b] = ld(min(base + b * MG_THREADS, tot - 1));
+#pragma unroll
+            for (int b = 0; b < MG_BATCH; ++b)
+                if (base + b * MG_THREADS < tot)
+                    st(base + b * MG_THREADS, v[b]);
+        }
+    };
+    // The E8M0 scale bytes of the workgroup's rows go to LDS once, in 2-byte
+    // units (CK is even): requested before the first code chunks, so they
+    // land first, and stored after the listing.  The main loop then reads one
+    // byte per chunk from LDS instead of a scattered global byte load next to
+    // each code load.
+    const int CKh = CK >> 1, stot = MG_ROWS * CKh;
+    auto sld = [&](int idx) {
+        const int rho = idx / CKh, u = idx - rho * CKh;
+        int c_, n_;
+        row_col(rho, c_, n_);
+        return *reinterpret_cast<const uint16_t *>(w_scale + ((size_t)ee * N + n_) * CK + 2 * u);
+    };
+    auto sst = [&](int idx, uint16_t v) {
+        const int rho = idx / CKh, u = idx - rho * CKh;
+        *reinterpret_cast<uint16_t *>(sl + (size_t)rho * CK + 2 * u) = v;
+    };
+    uint16_t sv[MG_SB];
+    if (e < E) {
+#pragma unroll
+        for (int b = 0; b < MG_SB; ++b)
+            sv[b] = sld(min(tid + b * MG_THREADS, stot - 1));
         fill();
+    }
     if (j0 >= p && b0 == e)
         list[atomicAdd(&count, 1)] = j0;
     if (j1 >= p && b1 == e)
@@ -629,7 +682,13 @@ __global__ __launch_bounds__(MG_THREADS) void moe_gemv_kernel(
         }
         return;
     }
-    const int K2 = 2 * K;
+#pragma unroll
+    for (int b = 0; b < MG_SB; ++b)
+        if (tid + b * MG_THREADS < stot)
+            sst(tid + b * MG_THREADS, sv[b]);
+    if (stot > MG_SB * MG_THREADS) // long rows: the rest, batched
+        stage(stot - MG_SB * MG_THREADS, [&](int idx) { return sld(idx + MG_SB * MG_THREADS); },
+              [&](int idx, uint16_t v) { sst(idx + MG_SB * MG_THREADS, v); });
     const int nv = K >> 3; // 16-byte blocks per activation row
     for (int m0 = 0; m0 < rows; m0 += MR) {
         const int mr = min(MR, rows - m0);
@@ -637,14 +696,19 @@ __global__ __launch_bounds__(MG_THREADS) void moe_gemv_kernel(
             __syncthreads(); // the previous pass's reads of the staged rows are done
             fill();
         }
-        for (int idx = tid; idx < mr * nv; idx += MG_THREADS) {
-            const int m = idx / nv, b = idx - m * nv;
-            const int tok = list[m0 + m] / topk;
-            reinterpret_cast<u32x4 *>(smem + (size_t)m * K2)[b] =
-                reinterpret_cast<const u32x4 *>(x + (size_t)tok * K)[b];
-        }
+        stage(
+            mr * nv,
+            [&](int idx) {
+                const int m = idx / nv, b = idx - m * nv;
+                const int tok = list[m0 + m] / topk;
+                return reinterpret_cast<const u32x4 *>(x + (size_t)tok * K)[b];
+            },
+            [&](int idx, const u32x4 &v) {
+                const int m = idx / nv, b = idx - m * nv;
+                reinterpret_cast<u32x4 *>(smem + (size_t)m * K2)[b] = v;
+            });
         __syncthreads();
-        mg_pass<ACT, MR>(wr, rw, rs, smem, K2, list + m0, mr, col, cvalid, lane, y, Nout);
+        mg_pass<ACT, MR>(wr, rw, smem, K2, list + m0, mr, col, cvalid, lane, y, Nout);
     }
 }
 
@@ -663,7 +727,8 @@ hipError_t launch_gemv(const void *x, const int32_t *ids, const uint8_t *w_fp4,
     const int64_t grid = (int64_t)P * n_slices; // one slot per pair; non-first pairs exit
     if (P > MG_PMAX || grid > INT32_MAX)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(MG_THREADS), (size_t)MR * 2 * (size_t)K,
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(MG_THREADS),
+                       (size_t)MR * 2 * (size_t)K + (size_t)mg_scale_bytes(K),
                        stream, static_cast<const uint16_t *>(x), ids, w_fp4, w_scale,
                        static_cast<uint16_t *>(y), P, topk, E, N, K, n_slices);
     return hipGetLastError();
