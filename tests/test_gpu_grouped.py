@@ -56,6 +56,13 @@ def test_grouped_ragged(wob, oracle, dtype, rows):
 
 
 @pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+def test_grouped_g128_scale_batches(wob, oracle, dtype):
+    # g = 128, G = 6: each group's tiles take the scales of four spans per load
+    d = wl.w4a16_grouped_inputs([70, 0, 300, 9], 264, 768, 128, dtype, seed=5)
+    _check(oracle, d, _run(wob, d))
+
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
 def test_grouped_many_groups_symmetric(wob, oracle, dtype):
     rng = np.random.default_rng(1)
     rows = list(rng.integers(0, 40, 100))

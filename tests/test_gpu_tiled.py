@@ -64,6 +64,19 @@ def test_tiled_shapes(wob, oracle, dtype, g, N, K):
     _check(oracle, d, _run(wob, d, wob.PATH_TILED))
 
 
+# g = 128 with an even number of groups G >= 4: the scales of four spans come
+# from one load; G = 6 and 10 end on a batch that overlaps the one before it,
+# G = 8 does not.  Ragged M and N, asymmetric and symmetric codes.
+G128_BATCHED = [(300, 520, 768), (40, 264, 1280), (129, 1024, 1024), (17, 24, 1280)]
+
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("M,N,K", G128_BATCHED)
+def test_tiled_g128_scale_batches(wob, oracle, dtype, M, N, K):
+    d = wl.w4a16_inputs(M, N, K, 128, dtype, seed=M + N + K, symmetric=(N == 24))
+    _check(oracle, d, _run(wob, d, wob.PATH_TILED))
+
+
 @pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
 def test_tiled_symmetric_and_signed(wob, oracle, dtype):
     d = wl.w4a16_inputs(70, 512, 512, 64, dtype, seed=5, symmetric=True)

@@ -143,8 +143,10 @@ __device__ __forceinline__ void dispatch_tile(int mb, const Fmt &fmt, const Cont
 }
 
 // m_offsets == nullptr: dense problem of M rows (n_mt tiles of TM_MAX rows).
-// GW: group size >= 64 (one scale / zero-point load per slice pair).
-template <int DT, int NB, bool HAS_Z, bool GW>
+// GM: group mode of the W4A16 format (0: g = 32; 1: g >= 64, one scale /
+// zero-point load per slice pair; 2: g = 128 with an even G >= 4, scales of
+// four spans per load).
+template <int DT, int NB, bool HAS_Z, int GM>
 __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
     const uint16_t *__restrict__ x, const uint32_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint32_t *__restrict__ qzeros,
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
     const int n0 = nt * GEO::TN;
     const int G = K >> (5 + gshift);
     const TileLane<> tl;
-    const FmtW4<DT, HAS_Z, NB, GW> fmt(qweight + (size_t)e * N * (K >> 3),
+    const FmtW4<DT, HAS_Z, NB, GM> fmt(qweight + (size_t)e * N * (K >> 3),
                                    scales + (size_t)e * N * G,
                                    HAS_Z ? qzeros + (size_t)e * (N >> 3) * G : qzeros, N, K,
                                    gshift, n0, tl);
@@ -199,12 +201,12 @@ __global__ __launch_bounds__(TL_THREADS, 1) void w4a16_tiled_kernel(
     dispatch_tile<DT, NB, GEO::MB_MAX>((rows + 31) >> 5, fmt, rws, xbase, K, N, n0, smem, tl);
 }
 
-template <int DT, int NB, bool HAS_Z, bool GW>
+template <int DT, int NB, bool HAS_Z, int GM>
 hipError_t launch_k(const W4Args &a, const int64_t *m_offsets, int num_groups, int grid, int n_mt,
                     int n_nt, int nxcd, size_t lds, hipStream_t stream)
 {
     const int gshift = a.g == 32 ? 0 : a.g == 64 ? 1 : 2;
-    auto kern = w4a16_tiled_kernel<DT, NB, HAS_Z, GW>;
+    auto kern = w4a16_tiled_kernel<DT, NB, HAS_Z, GM>;
     static std::atomic<uint64_t> lds_set{0};
     if (const hipError_t e = lds_optin(reinterpret_cast<const void *>(kern),
                                        TileGeo<NB>::lds_bytes(TileGeo<NB>::MB_MAX), lds_set);
@@ -218,7 +220,7 @@ hipError_t launch_k(const W4Args &a, const int64_t *m_offsets, int num_groups, i
     return hipGetLastError();
 }
 
-template <int DT, bool HAS_Z, bool GW>
+template <int DT, bool HAS_Z, int GM>
 hipError_t launch_zg(const W4Args &a, const int64_t *m_offsets, int num_groups, hipStream_t stream)
 {
     using GEO = TileGeo<TILED_NB>;
@@ -230,7 +232,7 @@ hipError_t launch_zg(const W4Args &a, const int64_t *m_offsets, int num_groups, 
         const int n_mt = (a.M + TMX - 1) / TMX;
         const int mb = n_mt == 1 ? (a.M + 31) / 32 : GEO::MB_MAX;
         const int grid = nxcd * ((n_mt * n_nt + nxcd - 1) / nxcd);
-        return launch_k<DT, TILED_NB, HAS_Z, GW>(a, nullptr, 0, grid, n_mt, n_nt, nxcd,
+        return launch_k<DT, TILED_NB, HAS_Z, GM>(a, nullptr, 0, grid, n_mt, n_nt, nxcd,
                                                  (size_t)GEO::lds_bytes(mb), stream);
     }
     // Upper bound on the tiles of all groups: sum of ceil(rows_e / TMX).
@@ -238,15 +240,21 @@ hipError_t launch_zg(const W4Args &a, const int64_t *m_offsets, int num_groups, 
     const int64_t grid = (int64_t)nxcd * ((max_mt * n_nt + nxcd - 1) / nxcd);
     if (grid > INT_MAX)
         return hipErrorInvalidValue;
-    return launch_k<DT, TILED_NB, HAS_Z, GW>(a, m_offsets, num_groups, (int)grid, 0, n_nt, nxcd,
+    return launch_k<DT, TILED_NB, HAS_Z, GM>(a, m_offsets, num_groups, (int)grid, 0, n_nt, nxcd,
                                              (size_t)GEO::lds_bytes(GEO::MB_MAX), stream);
 }
 
 template <int DT, bool HAS_Z>
 hipError_t launch_z(const W4Args &a, const int64_t *m_offsets, int num_groups, hipStream_t stream)
 {
-    return a.g >= 64 ? launch_zg<DT, HAS_Z, true>(a, m_offsets, num_groups, stream)
-                     : launch_zg<DT, HAS_Z, false>(a, m_offsets, num_groups, stream);
+#ifndef WOB_TILE_S4
+#define WOB_TILE_S4 1
+#endif
+    const int G = (int)(a.K / a.g);
+    if (WOB_TILE_S4 && a.g == 128 && G % 2 == 0 && G >= 4)
+        return launch_zg<DT, HAS_Z, 2>(a, m_offsets, num_groups, stream);
+    return a.g >= 64 ? launch_zg<DT, HAS_Z, 1>(a, m_offsets, num_groups, stream)
+                     : launch_zg<DT, HAS_Z, 0>(a, m_offsets, num_groups, stream);
 }
 
 hipError_t launch_any(const W4Args &a, const int64_t *m_offsets, int num_groups, hipStream_t stream)

@@ -311,6 +311,7 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
     // flight; this span's `cur` is refilled for span + 2 once consumed.
     auto run_span = [&](int span, typename Fmt::Meta &cur) __attribute__((always_inline)) {
         const int buf = span & 1;
+        fmt.begin_span(span); // loads ahead of this span's copies (see the format)
         // The next span's tiles (the last span copies itself again: no branch
         // splits the step, and the copy is waited for before the last barrier).
         uint32_t kx, kw;
@@ -633,21 +634,34 @@ __device__ __forceinline__ int xcd_tile(int tiles, int nxcd)
 // n_nb = n0 + BR NB wave + BR nb + nl, which share n % 8, so one nibble shift
 // of the zero-point words serves all its blocks.  A lane's k of a span are
 // PPL 32-wide slices hf (k = 32 (PPL g + hf) ..), each inside one group.
-template <int DT, bool HAS_Z, int NB, bool GW, int BR = 32>
+// GM (group mode): 0 for g = 32; 1 for g >= 64; 2 for g = 128 with an even
+// number of groups G >= 4 per row.
+template <int DT, bool HAS_Z, int NB, int GM, int BR = 32>
 struct FmtW4 {
     static constexpr int PPL = TileGeo<NB, BR>::PPL;
     // GW: every group spans at least 64 k (g >= 64), so a lane's two 32-wide
     // slices of a span (BR = 32) share one scale and one zero-point word: one
     // load each.
+    static constexpr bool GW = GM >= 1;
+    // S4 (g = 128, BR = 32: a span is one group): a lane's scales of four
+    // consecutive spans are 8 contiguous bytes of its row, loaded together
+    // every four spans into `sb` (two dword loads per block, issued before the
+    // span's tile copies) instead of one 2-byte load per span, each of which
+    // touches a cache line per row of the block.
+    static constexpr bool S4 = GM == 2;
+    static_assert(!S4 || BR == 32, "a span is one group");
     static constexpr int LPS = GW ? 1 : PPL; // loads per block per span
-    static constexpr int NLOADS = NB * (HAS_Z ? 2 : 1) * LPS;
+    static constexpr int NLOADS = NB * ((HAS_Z ? 1 : 0) + (S4 ? 0 : 1)) * LPS;
     static constexpr bool ZERO_CODES = false; // slices past K: zero scales
     struct Meta {
         uint32_t s[NB][PPL], z[NB][PPL];
     };
     const uint8_t *wq, *ws, *wz;
     uint32_t soff[NB], zoff[NB];
-    int K, gshift, g, zsh;
+    int K, gshift, g, zsh, G;
+    // S4: scales of groups sb_base .. sb_base + 3 (binary16 pairs per block)
+    mutable uint32_t sb[NB][2];
+    mutable int sb_base;
 
     __device__ FmtW4(const uint32_t *qweight, const uint16_t *scales, const uint32_t *qzeros,
                      int N, int K_, int gshift_, int n0, const TileLane<BR> &tl)
@@ -659,12 +673,39 @@ struct FmtW4 {
         gshift = gshift_;
         g = tl.g;
         zsh = 4 * (tl.nl & 7);
-        const int G = K >> (5 + gshift);
+        G = K >> (5 + gshift);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int n = min(n0 + BR * NB * tl.wave + BR * nb + tl.nl, N - 1);
             soff[nb] = (uint32_t)n * (uint32_t)G * 2u;
             zoff[nb] = (uint32_t)(n >> 3) * (uint32_t)G * 4u;
+        }
+        if constexpr (S4)
+            load_batch(0);
+    }
+
+    // S4: the scales of groups b .. b + 3 (b = min(4 t, G - 4): inside the row).
+    // Rows are 2 G bytes (G even) and b is even, so both dwords are aligned.
+    __device__ __forceinline__ void load_batch(int b) const
+    {
+        sb_base = b;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const uint32_t *p = reinterpret_cast<const uint32_t *>(ws + soff[nb] + 2u * (uint32_t)b);
+            sb[nb][0] = p[0];
+            sb[nb][1] = p[1];
+        }
+    }
+
+    // Called at the start of every span, before its tile copies.  S4: span
+    // 4 t + 2 refills `sb` with the batch of spans 4 t + 4 .. 4 t + 7, whose
+    // meta load_meta reads from the end of that span on; the last read of the
+    // previous batch (meta of span 4 t + 3) happened at the end of span 4 t + 1.
+    __device__ __forceinline__ void begin_span(int span) const
+    {
+        if constexpr (S4) {
+            if ((span & 3) == 2)
+                load_batch(min(4 * ((span >> 2) + 1), G - 4));
         }
     }
 
@@ -679,7 +720,14 @@ struct FmtW4 {
             const uint32_t grp = (uint32_t)(kc >> (5 + gshift));
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                m.s[nb][hf] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + 2u * grp);
+                if constexpr (S4) {
+                    // group `span` (< G: the caller clamps the span) of the batch
+                    const int idx = span - sb_base;
+                    const uint32_t w2 = (idx & 2) ? sb[nb][1] : sb[nb][0];
+                    m.s[nb][hf] = (idx & 1) ? w2 >> 16 : w2 & 0xFFFFu;
+                } else {
+                    m.s[nb][hf] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + 2u * grp);
+                }
                 m.z[nb][hf] = HAS_Z ? *reinterpret_cast<const uint32_t *>(wz + zoff[nb] + 4u * grp)
                                     : 0x88888888u;
             }
@@ -763,6 +811,8 @@ struct FmtFP4 {
                    min(n0 + (BR * NB / 2) * w + BR * (nb >> 1) + (t & (BR - 1)), half - 1);
         }
     }
+
+    __device__ __forceinline__ void begin_span(int) const {}
 
     __device__ __forceinline__ void load_meta(int span, Meta &m) const
     {
