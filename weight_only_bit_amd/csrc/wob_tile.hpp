@@ -312,6 +312,7 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
     auto run_span = [&](int span, typename Fmt::Meta &cur) __attribute__((always_inline)) {
         const int buf = span & 1;
         fmt.begin_span(span); // loads ahead of this span's copies (see the format)
+        Fmt::pin(cur);        // (see the format)
         // The next span's tiles (the last span copies itself again: no branch
         // splits the step, and the copy is waited for before the last barrier).
         uint32_t kx, kw;
@@ -656,8 +657,31 @@ struct FmtW4 {
     struct Meta {
         uint32_t s[NB][PPL], z[NB][PPL];
     };
+    // bfloat16, g = 32: the span's meta (loaded at the end of span - 2) is
+    // pinned at the start of its span (no instruction), so the compiler
+    // cannot compute its zero-point bias pairs and scales at the start of
+    // span - 1, right after the barrier that follows the loads, where that
+    // waited for them.  (Pinned in binary16, or with g = 128, the loads went
+    // through copies placed at the same spot instead.)
+    __device__ __forceinline__ static void pin(Meta &m)
+    {
+        if constexpr (SDW) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int hf = 0; hf < PPL; ++hf)
+                    asm volatile("" : "+v"(m.s[nb][hf]), "+v"(m.z[nb][hf]));
+        }
+    }
     const uint8_t *wq, *ws, *wz;
     uint32_t soff[NB], zoff[NB];
+    // bfloat16 with g = 32: each scale is loaded as the aligned dword holding
+    // it, so the value stays 32 bits wide (a 2-byte load was narrowed and
+    // widened again right after the span barrier, which waited for the load
+    // there).  ssh: bit offset of slice 0's scale in its dword, the same for
+    // every span (its group 4 span + 2 g is even); slice 1's is 16 - ssh.
+    static constexpr bool SDW = DT == DT_BF16 && GM == 0;
+    uint32_t ssh[NB];
     int K, gshift, g, zsh, G;
     // S4: scales of groups sb_base .. sb_base + 3 (binary16 pairs per block)
     mutable uint32_t sb[NB][2];
@@ -679,6 +703,7 @@ struct FmtW4 {
             const int n = min(n0 + BR * NB * tl.wave + BR * nb + tl.nl, N - 1);
             soff[nb] = (uint32_t)n * (uint32_t)G * 2u;
             zoff[nb] = (uint32_t)(n >> 3) * (uint32_t)G * 4u;
+            ssh[nb] = 16u * ((soff[nb] >> 1) & 1u);
         }
         if constexpr (S4)
             load_batch(0);
@@ -725,6 +750,9 @@ struct FmtW4 {
                     const int idx = span - sb_base;
                     const uint32_t w2 = (idx & 2) ? sb[nb][1] : sb[nb][0];
                     m.s[nb][hf] = (idx & 1) ? w2 >> 16 : w2 & 0xFFFFu;
+                } else if constexpr (SDW) {
+                    // In bounds: the scale array is a multiple of 16 bytes.
+                    m.s[nb][hf] = *reinterpret_cast<const uint32_t *>(ws + ((soff[nb] + 2u * grp) & ~3u));
                 } else {
                     m.s[nb][hf] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + 2u * grp);
                 }
@@ -756,7 +784,10 @@ struct FmtW4 {
     {
         const int hf = st >> 2;
         const uint32_t z = (m.z[nb][hf] >> zsh) & 0xFu;
-        return w4_word_act8<DT>(word, m.s[nb][hf], z);
+        uint32_t sbits = m.s[nb][hf];
+        if constexpr (SDW)
+            sbits >>= hf == 0 ? ssh[nb] : 16u - ssh[nb];
+        return w4_word_act8<DT>(word, sbits, z);
     }
 };
 
@@ -777,10 +808,14 @@ struct FmtFP4 {
     static constexpr int NLOADS = NB;
     static constexpr bool ZERO_CODES = true; // slices past K: zero codes
     struct Meta {
-        uint32_t s[NB]; // E8M0 bytes of slices hf = 0 (low byte) and 1 (BR = 32)
+        // BR = 32: the aligned dword holding the lane's E8M0 pair (slices
+        // hf = 0, 1 at bytes sh / 8, sh / 8 + 1); BR = 16: the byte
+        uint32_t s[NB];
     };
+    __device__ __forceinline__ static void pin(Meta &) {}
     const uint8_t *wq, *ws;
     uint32_t soff[NB];
+    uint32_t sh[NB]; // BR = 32: bit offset of the pair in its dword (0 or 16)
     int K, g;
 
     __device__ FmtFP4(const uint8_t *w_fp4, const uint8_t *w_scale, int N, int K_, int n0,
@@ -794,6 +829,9 @@ struct FmtFP4 {
         for (int nb = 0; nb < NB; ++nb) {
             const int n = tile_row(n0, N, BR * NB * tl.wave + BR * nb + tl.nl);
             soff[nb] = (uint32_t)n * (uint32_t)(K >> 5);
+            // The pair's address soff + 4 span + 2 g is even; its dword starts
+            // 0 or 2 bytes before it, the same for every span of the lane.
+            sh[nb] = 8u * ((soff[nb] + 2u * (uint32_t)g) & 2u);
         }
     }
 
@@ -821,8 +859,13 @@ struct FmtFP4 {
         const uint32_t kg = (uint32_t)k >> 5; // even when PPL = 2
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
+            // BR = 32: the whole aligned dword, so the value stays 32 bits wide
+            // (a 2-byte load was narrowed and widened again right after the
+            // span barrier, which waited for the load there).  In bounds: the
+            // scale array is a multiple of 32 bytes, so a pair at a multiple
+            // of 4 is never its last 2 bytes.
             if constexpr (PPL == 2)
-                m.s[nb] = *reinterpret_cast<const uint16_t *>(ws + soff[nb] + kg);
+                m.s[nb] = *reinterpret_cast<const uint32_t *>(ws + soff[nb] + kg - sh[nb] / 8u);
             else
                 m.s[nb] = ws[soff[nb] + kg];
         }
@@ -843,7 +886,8 @@ struct FmtFP4 {
     __device__ __forceinline__ u32x4 dequant(uint32_t word, const Meta &m, int nb, int st) const
     {
         const int hf = st >> 2;
-        const float scale = e8m0_to_f32((m.s[nb] >> (8 * hf)) & 0xFFu);
+        const uint32_t bit = PPL == 2 ? sh[nb] + 8u * (uint32_t)hf : 0u;
+        const float scale = e8m0_to_f32((m.s[nb] >> bit) & 0xFFu);
         return fp4_word_bf16x8(word, scale);
     }
 };
