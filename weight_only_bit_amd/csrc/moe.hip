@@ -72,6 +72,7 @@ static_assert(moe_tm<false, 32>() >= MOE_TM_MIN && moe_tm<true, 32>() >= MOE_TM_
                   moe_tm<false, 16>() >= MOE_TM_MIN && moe_tm<true, 16>() >= MOE_TM_MIN,
               "workspace bound");
 constexpr int ROUTE_THREADS = 1024;
+constexpr int ROUTE_IPT = 4; // ids per thread per batch (P = 4096 in one)
 
 struct MoeWs {
     int32_t *hdr;    // [0]: number of expert tiles
@@ -106,11 +107,25 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const int32_t 
     for (int e = tid; e <= E; e += ROUTE_THREADS)
         cnt[e] = 0;
     __syncthreads();
-    for (int i = tid; i < P; i += ROUTE_THREADS) {
-        int e = ids[i];
-        if ((unsigned)e >= (unsigned)E)
-            e = E;
-        atomicAdd(&cnt[e], 1);
+    // The ids are read ROUTE_IPT per thread at a time, all requested before
+    // any is used (a loop of one load and one LDS atomic waited a full memory
+    // round trip per id), and with P <= ROUTE_IPT x ROUTE_THREADS kept in
+    // registers for the scatter below.
+    auto bucket = [&](int e) { return (unsigned)e < (unsigned)E ? e : E; };
+    int eb[ROUTE_IPT];
+    for (int base = 0; base < P; base += ROUTE_IPT * ROUTE_THREADS) {
+        int v[ROUTE_IPT];
+#pragma unroll
+        for (int b = 0; b < ROUTE_IPT; ++b) {
+            const int i = base + b * ROUTE_THREADS + tid;
+            v[b] = ids[min(i, P - 1)]; // unconditional (clamped): issued together
+        }
+#pragma unroll
+        for (int b = 0; b < ROUTE_IPT; ++b) {
+            eb[b] = bucket(v[b]);
+            if (base + b * ROUTE_THREADS + tid < P)
+                atomicAdd(&cnt[eb[b]], 1);
+        }
     }
     __syncthreads();
 
@@ -156,11 +171,30 @@ __global__ __launch_bounds__(ROUTE_THREADS) void moe_route_kernel(const int32_t 
         cnt[e] = 0;
     }
     __syncthreads();
-    for (int i = tid; i < P; i += ROUTE_THREADS) {
-        int e = ids[i];
-        if ((unsigned)e >= (unsigned)E)
-            e = E;
-        sorted[off[e] + atomicAdd(&cnt[e], 1)] = i;
+    if (P <= ROUTE_IPT * ROUTE_THREADS) {
+#pragma unroll
+        for (int b = 0; b < ROUTE_IPT; ++b) {
+            const int i = b * ROUTE_THREADS + tid;
+            if (i < P)
+                sorted[off[eb[b]] + atomicAdd(&cnt[eb[b]], 1)] = i;
+        }
+        return;
+    }
+    for (int base = 0; base < P; base += ROUTE_IPT * ROUTE_THREADS) {
+        int v[ROUTE_IPT];
+#pragma unroll
+        for (int b = 0; b < ROUTE_IPT; ++b) {
+            const int i = base + b * ROUTE_THREADS + tid;
+            v[b] = ids[min(i, P - 1)]; // unconditional (clamped): issued together
+        }
+#pragma unroll
+        for (int b = 0; b < ROUTE_IPT; ++b) {
+            const int i = base + b * ROUTE_THREADS + tid;
+            if (i < P) {
+                const int e = bucket(v[b]);
+                sorted[off[e] + atomicAdd(&cnt[e], 1)] = i;
+            }
+        }
     }
 }
 
