@@ -68,7 +68,10 @@ def test_skinny_parity_matrix(wob, oracle, dtype, g, N, K, M):
 
 @pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
 @pytest.mark.parametrize("M,N,K,g", [(1, 8, 32, 32), (3, 16, 96, 32), (4, 24, 160, 32),
-                                     (2, 40, 384, 128), (8, 64, 1088, 64), (1, 4104, 4096, 128)])
+                                     (2, 40, 384, 128), (8, 64, 1088, 64), (1, 4104, 4096, 128),
+                                     # 2049 octets, K split 2 ways over 8-wave workgroups of
+                                     # 4 octets: the last workgroup holds one octet
+                                     (1, 16392, 2048, 32), (3, 16392, 1024, 128)])
 def test_skinny_ragged_shapes(wob, oracle, dtype, M, N, K, g):
     d = wl.w4a16_inputs(M, N, K, g, dtype, seed=N + K)
     _check(oracle, d, _run(wob, d, wob.PATH_SKINNY))
