@@ -247,11 +247,9 @@ hipError_t launch_zg(const W4Args &a, const int64_t *m_offsets, int num_groups, 
 template <int DT, bool HAS_Z>
 hipError_t launch_z(const W4Args &a, const int64_t *m_offsets, int num_groups, hipStream_t stream)
 {
-#ifndef WOB_TILE_S4
-#define WOB_TILE_S4 1
-#endif
+    // g = 128 with an even G >= 4: the scales of four spans per load (GM 2)
     const int G = (int)(a.K / a.g);
-    if (WOB_TILE_S4 && a.g == 128 && G % 2 == 0 && G >= 4)
+    if (a.g == 128 && G % 2 == 0 && G >= 4)
         return launch_zg<DT, HAS_Z, 2>(a, m_offsets, num_groups, stream);
     return a.g >= 64 ? launch_zg<DT, HAS_Z, 1>(a, m_offsets, num_groups, stream)
                      : launch_zg<DT, HAS_Z, 0>(a, m_offsets, num_groups, stream);

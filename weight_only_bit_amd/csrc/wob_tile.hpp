@@ -76,6 +76,9 @@
 //    BR NB w + BR nb + nl)
 //    struct Meta;                         a lane's scales / zero-points of a span
 //    static constexpr int NLOADS;         vector-memory operations per load_meta()
+//    void begin_span(int span) const;     at a span's start, before its copies
+//                                         (loads issued here are older than them)
+//    static void pin(Meta &m);            at a span's start, on that span's meta
 //    void load_meta(int span, Meta &m) const;
 //    void zero_past_k(int span, u32x4 (&cw)[NB][PPL], Meta &m) const;
 //                                         weights of slices past K -> 0 (codes or scales)
