@@ -819,6 +819,15 @@ struct FmtFP4 {
     const uint8_t *wq, *ws;
     uint32_t soff[NB];
     uint32_t sh[NB]; // BR = 32: bit offset of the pair in its dword (0 or 16)
+    // BR = 32: the lane reads the pair of lane group gs (its own group g,
+    // except at K = 64, where group 1 has no pair inside K and reads group
+    // 0's), up to span slast, the last with that pair inside K; later spans
+    // reuse that dword (their codes are zero).  Clamping the span, not k,
+    // keeps the pair's offset in its dword: a pair clamped to the row's last
+    // k of the other lane group sat 2 bytes off, which made the load
+    // unaligned and 2 bytes past the row (past the array on its last row, and
+    // before it on its first row at K = 64).
+    int gs, slast;
     int K, g;
 
     __device__ FmtFP4(const uint8_t *w_fp4, const uint8_t *w_scale, int N, int K_, int n0,
@@ -828,13 +837,15 @@ struct FmtFP4 {
         ws = w_scale;
         K = K_;
         g = tl.g;
+        gs = K >= 128 ? g : 0;
+        slast = ((K >> 5) - 2 - 2 * gs) >> 2; // pair 4 s + 2 gs <= K / 32 - 2
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int n = tile_row(n0, N, BR * NB * tl.wave + BR * nb + tl.nl);
             soff[nb] = (uint32_t)n * (uint32_t)(K >> 5);
-            // The pair's address soff + 4 span + 2 g is even; its dword starts
+            // The pair's address soff + 4 span + 2 gs is even; its dword starts
             // 0 or 2 bytes before it, the same for every span of the lane.
-            sh[nb] = 8u * ((soff[nb] + 2u * (uint32_t)g) & 2u);
+            sh[nb] = 8u * ((soff[nb] + 2u * (uint32_t)gs) & 2u);
         }
     }
 
@@ -857,20 +868,21 @@ struct FmtFP4 {
 
     __device__ __forceinline__ void load_meta(int span, Meta &m) const
     {
-        // past K: clamped, zeroed later
-        const int k = min(span * TL_SPAN + 32 * PPL * g, K - 32 * PPL);
-        const uint32_t kg = (uint32_t)k >> 5; // even when PPL = 2
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             // BR = 32: the whole aligned dword, so the value stays 32 bits wide
             // (a 2-byte load was narrowed and widened again right after the
             // span barrier, which waited for the load there).  In bounds: the
-            // scale array is a multiple of 32 bytes, so a pair at a multiple
-            // of 4 is never its last 2 bytes.
-            if constexpr (PPL == 2)
+            // pair lies in the row and the scale array is a multiple of 32
+            // bytes, so a pair at a multiple of 4 is never its last 2 bytes.
+            if constexpr (PPL == 2) {
+                const uint32_t kg = 4u * (uint32_t)min(span, slast) + 2u * (uint32_t)gs;
                 m.s[nb] = *reinterpret_cast<const uint32_t *>(ws + soff[nb] + kg - sh[nb] / 8u);
-            else
-                m.s[nb] = ws[soff[nb] + kg];
+            } else {
+                // past K: clamped to the row's last byte, zeroed codes
+                const int k = min(span * TL_SPAN + 32 * g, K - 32);
+                m.s[nb] = ws[soff[nb] + ((uint32_t)k >> 5)];
+            }
         }
     }
 
