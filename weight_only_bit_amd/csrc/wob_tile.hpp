@@ -213,6 +213,12 @@ struct TileLane {
     }
 };
 
+// Compile-time tag of a K-loop span: the tail span (last of an odd count) or not.
+template <bool TAIL>
+struct SpanTail {
+    static constexpr bool value = TAIL;
+};
+
 // First activation row of DMA instruction i for this lane is row 16 i + rl.
 // `XRows` supplies the byte offset (from `xbase`) of activation row r of the
 // tile, already clamped to a valid row:  uint32_t XRows::off(int i) const
@@ -312,7 +318,9 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
     // One span: MFMAs on LDS buffers span & 1 with the scales in `cur`.  At
     // entry the next span's scales (the other buffer) have landed or are in
     // flight; this span's `cur` is refilled for span + 2 once consumed.
-    auto run_span = [&](int span, typename Fmt::Meta &cur) __attribute__((always_inline)) {
+    // TAIL: the last span of an odd span count, run after the paired loop
+    // (see the end of the span).
+    auto run_span = [&](int span, typename Fmt::Meta &cur, auto tail) __attribute__((always_inline)) {
         const int buf = span & 1;
         fmt.begin_span(span); // loads ahead of this span's copies (see the format)
         Fmt::pin(cur);        // (see the format)
@@ -475,22 +483,30 @@ __device__ __forceinline__ void tile_mainloop(const Fmt &fmt, const XRows &xr,
         // `cur` is consumed: refill it for span + 2 (clamped, so the wait
         // counts stay exact), then the barrier that publishes the next tiles:
         // wait for everything but that refill (next activation and code
-        // tiles + the next span's scales).
-        fmt.load_meta(min(span + 2, S - 1), cur);
-        wait_vmcnt<Fmt::NLOADS>();
+        // tiles + the next span's scales).  The tail span refills nothing and
+        // waits for everything: its refill would be dead, the compiler drops
+        // dead loads, and the count of NLOADS would then leave that many of
+        // the span's copies in flight past the last barrier, landing in LDS
+        // the epilogue has already reused (staged outputs, row indices).
+        if constexpr (decltype(tail)::value) {
+            wait_vmcnt<0>();
+        } else {
+            fmt.load_meta(min(span + 2, S - 1), cur);
+            wait_vmcnt<Fmt::NLOADS>();
+        }
         barrier_only();
     };
 
     int span = 0;
     for (; span + 1 < S; span += 2) {
-        run_span(span, mA);
-        run_span(span + 1, mB);
+        run_span(span, mA, SpanTail<false>{});
+        run_span(span + 1, mB, SpanTail<false>{});
     }
     if (span < S)
-        run_span(span, mA);
-    // Only the last (clamped, duplicate) scale refill can still be in flight
-    // here; it targets registers, which the compiler's own wait counts cover.
-    // Every copy into LDS has been waited for.
+        run_span(span, mA, SpanTail<true>{});
+    // Only the last pair's (clamped, duplicate) scale refills can still be in
+    // flight here; they target registers, which the compiler's own wait
+    // counts cover.  Every copy into LDS has been waited for.
 }
 
 // Store one tile's accumulators through LDS, so that every global store
